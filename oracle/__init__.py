@@ -1,0 +1,22 @@
+"""Plain FP64 CPU oracle of the paired-4:8 sparse NVFP4 (W4A4) MoE expert path.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product (the ``sparse_quantized_moe_amd`` package, its HIP
+library or its C ABI) may import, call or link this package; only ``tests/``, the smoke check and the
+bench's CPU-baseline leg do. It shares no code, table or constant generator with the HIP library.
+
+What it states, each function citing the passage it follows:
+
+* ``nvfp4``      E2M1 / E4M3FN codecs and the per-32 NVFP4 quantizer (model cards, "Compression details").
+* ``pairbitmask`` the pair-bitmask storage codec (model cards, "Sparse storage layout").
+* ``compress``   synthetic weight compression: paired-4:8 magnitude prune, NVFP4, pack.
+* ``moe``        the token->expert permutation, the grouped GEMM and the MoE FFN with top-k combine.
+
+Every value is computed in float64 from exact inputs; see each docstring for why that reaches the exact
+decision where an integer (a code or a scale byte) is decided by a real-valued comparison.
+
+Parity status: the codecs, the quantizer, the codec of the storage format, the prune, the permutation
+and the grouped GEMM are pinned by tests against textbook tables, a library cast, exact-rational brute
+force, hand-derived fixtures and the pages' storage figures. The end-to-end FFN is a composition of
+pinned stages plus libm ``exp`` and is otherwise pinned only by metamorphic relations.
+"""
+from . import nvfp4, pairbitmask, compress, moe  # noqa: F401

@@ -1,0 +1,138 @@
+"""Pins of the oracle's permutation, grouped GEMM and FFN (no GPU): brute force, exact rationals,
+library reductions and metamorphic relations."""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import compress, moe, nvfp4, pairbitmask
+import synth
+
+
+def test_permute_vs_brute_force():
+    rng = np.random.default_rng(0)
+    T, k, E = 37, 4, 9
+    ids = rng.integers(-1, E, size=(T, k))
+    ids[3, :] = [2, 2, 5, -1]                       # a duplicate id counts twice; -1 is dropped
+    counts, offsets, sorted_pairs, inv = moe.permute(ids, E)
+    brute = [t * k + j for e in range(E) for t in range(T) for j in range(k) if ids[t, j] == e]
+    assert sorted_pairs.tolist() == brute
+    assert counts.tolist() == [int((ids == e).sum()) for e in range(E)]
+    assert offsets[0] == 0 and offsets[-1] == len(brute) and (np.diff(offsets) == counts).all()
+    for p in range(T * k):
+        assert (inv[p] == -1) == (ids.ravel()[p] == -1)
+        if inv[p] >= 0:
+            assert sorted_pairs[inv[p]] == p
+    with pytest.raises(ValueError):
+        moe.permute(np.array([[E]]), E)
+
+
+def _exact_value(code, sbyte, g):
+    return Fraction(float(nvfp4.e2m1_decode(code))) * Fraction(float(nvfp4.e4m3fn_decode(sbyte))) * Fraction(float(g))
+
+
+def test_grouped_gemm_vs_exact_rationals():
+    """Two experts, tiny shapes: every output against an exact rational sum."""
+    E, N, K = 2, 6, 64
+    packed, mask, scale, gw = synth.random_sparse_weights(3, E, N, K, G=2)
+    a_codes, a_scales = synth.random_act_codes(4, 5, K)
+    a_scales = np.clip(a_scales, 0x20, 0x5F)
+    a_global = np.array([0.011, 0.37], np.float32)
+    offsets = np.array([0, 2, 5])
+    out = moe.grouped_gemm(a_codes, a_scales, a_global, offsets, packed, mask, scale, gw)
+    ac = nvfp4.unpack_codes(a_codes)
+    for e in range(E):
+        dense = pairbitmask.unpack(packed[e], mask[e])
+        wc = nvfp4.unpack_codes(dense)
+        for r in range(offsets[e], offsets[e + 1]):
+            for n in range(N):
+                g_w = gw[e, 0] if n < N // 2 else gw[e, 1]
+                acc = Fraction(0)
+                mag = Fraction(0)
+                for kk in range(K):
+                    term = _exact_value(ac[r, kk], a_scales[r, kk // 32], a_global[e]) * \
+                        _exact_value(wc[n, kk], scale[e, n, kk // 32], g_w)
+                    acc += term
+                    mag += abs(term)
+                # float64 summation of K exact-ish products: error <= K * 2^-53 * sum|terms|
+                assert abs(Fraction(float(out[r, n])) - acc) <= Fraction(K, 2 ** 53) * mag, (e, r, n)
+
+
+def test_grouped_gemm_single_expert_is_matmul_of_dequantized():
+    N, K, M = 16, 128, 9
+    packed, mask, scale, gw = synth.random_sparse_weights(5, 1, N, K)
+    a_codes, a_scales = synth.random_act_codes(6, M, K)
+    out = moe.grouped_gemm(a_codes, a_scales, [0.5], [0, M], packed, mask, scale, gw)
+    W = compress.decompress(packed[0], mask[0], scale[0], gw[0, 0])
+    X = nvfp4.dequantize(a_codes, a_scales, 0.5)
+    assert np.allclose(out, np.matmul(X, W.T), rtol=1e-13, atol=0)
+
+
+def _tiny_layer(seed, E, H, I):
+    w13 = [[], [], [], []]
+    w2 = [[], [], [], []]
+    for e in range(E):
+        g, u, d = synth.expert_dense_weights(seed, e, H, I)
+        pg, mg, sg, gg = compress.compress(g.numpy())
+        pu, mu, su, gu = compress.compress(u.numpy())
+        for lst, vals in zip(w13, [np.concatenate([pg, pu]), np.concatenate([mg, mu]),
+                                   np.concatenate([sg, su]), np.array([gg, gu], np.float32)]):
+            lst.append(vals)
+        for lst, vals in zip(w2, compress.compress(d.numpy())):
+            lst.append(vals if np.ndim(vals) else np.array([vals], np.float32))
+    return [np.stack(v) for v in w13], [np.stack(v) for v in w2]
+
+
+def test_ffn_top1_equals_single_expert_and_is_equivariant():
+    E, H, I, T = 3, 64, 32, 12
+    w13, w2 = _tiny_layer(9, E, H, I)
+    x = synth.activations(1, T, H).float().numpy()
+    g13 = np.full(E, np.float32(0.002), np.float32)
+    g2 = np.full(E, np.float32(0.0005), np.float32)
+    ids = np.array([[t % E] for t in range(T)], np.int32)
+    wts = np.ones((T, 1), np.float32)
+    out = moe.moe_ffn(x, ids, wts, w13, w2, g13, g2)
+    # single-expert FFN of token t through its expert, written out stage by stage
+    for t in range(T):
+        e = t % E
+        c, s = nvfp4.quantize(x[t:t + 1], g13[e])
+        W13 = moe.dequant_weight(w13[0][e], w13[1][e], w13[2][e], w13[3][e])
+        gu = nvfp4.dequantize(c, s, g13[e]) @ W13.T
+        h = gu[:, :I] / (1 + np.exp(-gu[:, :I])) * gu[:, I:]
+        c2, s2 = nvfp4.quantize(h, g2[e])
+        y = nvfp4.dequantize(c2, s2, g2[e]) @ moe.dequant_weight(w2[0][e], w2[1][e], w2[2][e], w2[3][e]).T
+        assert np.allclose(out[t], y[0], rtol=1e-12, atol=1e-15)
+    # shuffling tokens permutes the output rows
+    perm = np.random.default_rng(0).permutation(T)
+    out_p = moe.moe_ffn(x[perm], ids[perm], wts[perm], w13, w2, g13, g2)
+    assert np.allclose(out_p, out[perm], rtol=1e-13, atol=1e-16)
+
+
+def test_ffn_topk_is_weighted_sum_of_top1():
+    E, H, I, T, k = 4, 64, 32, 6, 3
+    w13, w2 = _tiny_layer(10, E, H, I)
+    x = synth.activations(2, T, H).float().numpy()
+    ids, wts = synth.routing(3, T, E, k)
+    g13 = np.full(E, np.float32(0.002), np.float32)
+    g2 = np.full(E, np.float32(0.0005), np.float32)
+    out = moe.moe_ffn(x, ids, wts, w13, w2, g13, g2)
+    acc = np.zeros_like(out)
+    for j in range(k):
+        acc += moe.moe_ffn(x, ids[:, j:j + 1], wts[:, j:j + 1], w13, w2, g13, g2)
+    assert np.allclose(out, acc, rtol=1e-12, atol=1e-15)
+    # dropping a pair (-1) removes exactly its term
+    ids2 = ids.copy()
+    ids2[:, 2] = -1
+    out2 = moe.moe_ffn(x, ids2, wts, w13, w2, g13, g2)
+    out_j2 = moe.moe_ffn(x, ids[:, 2:3], wts[:, 2:3], w13, w2, g13, g2)
+    assert np.allclose(out2 + out_j2, out, rtol=1e-12, atol=1e-15)
+
+
+def test_synth_routing_shapes():
+    w = synth.WORKLOADS["qwen3_30b_prefill"]
+    ids, wts = synth.routing(0, w.T, w.E, w.k, w.routing, w.zipf_s, w.zipf_beta)
+    counts = np.bincount(ids.ravel(), minlength=128)
+    assert counts.max() > 5 * counts.mean() and (counts == 0).sum() >= 1
+    assert np.allclose(wts.sum(axis=1), 1, atol=1e-6)
+    assert (np.diff(np.sort(ids, axis=1), axis=1) > 0).all()        # distinct experts per token
