@@ -1,0 +1,164 @@
+/*
+ * moesq: paired-4:8 sparse NVFP4 (W4A4) MoE expert path for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI. Every pointer is a DEVICE pointer unless its comment says "host". Every call that takes a
+ * hipStream_t is asynchronous on that stream: it validates its arguments on the host, enqueues its
+ * kernels and returns; kernel faults surface at the caller's next synchronization (or inside the call
+ * with MOESQ_FLAG_SYNC_CHECK). The library never allocates or frees device memory in these calls and
+ * keeps no pointer after return; the caller owns every buffer, including workspaces, and keeps it
+ * alive until the stream work is done. No C++ exception crosses this boundary. The calls keep no
+ * global mutable state apart from a one-time kernel attribute set-up and the thread-local text of
+ * moesq_last_error(), so they are reentrant.
+ *
+ * Errors: a synchronous argument check returns a negative moesq_status and enqueues nothing; a launch
+ * failure returns MOESQ_ERR_HIP with the HIP error text in moesq_last_error().
+ *
+ * Storage format (model card "Qwen3.5-397B-A17B-P48NVFP4-MoESQ", section "Sparse storage layout",
+ * table of stored tensors): per expert linear [out = N, in = K]
+ *   packed u8 [N][K/4]   the 2 kept bytes of every 4-byte chunk of packed NVFP4, in K order;
+ *   mask   u8 [N][K/16]  one nibble per 4-byte chunk, exactly 2 bits set, bit i = byte i kept,
+ *                        the lower-K chunk in the low nibble;
+ *   scale  u8 [N][K/32]  FP8-E4M3 (OCP, "FN") block scales, row-major ("linear layout");
+ *   global f32           per-tensor scale, multiplicative: value = e2m1(code) * e4m3(scale) * global.
+ * Packed NVFP4 holds two adjacent K per byte, the lower K in the low nibble. Activation NVFP4 (model
+ * card "Compression details"): per 32 K an E4M3 scale = RNE(amax / (6 * global)) saturating at 448,
+ * codes = RNE(x / (scale * global)) saturating at 6, ties to even, sign copied from x; global is the
+ * FP32 "input_global_scale" stored per expert linear.
+ */
+#ifndef MOESQ_H_
+#define MOESQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOESQ_ABI_VERSION 1
+/* quantization_config marker "paired48_sparse": {"layout": "pair-bitmask", "version": 1} */
+#define MOESQ_PAIR_BITMASK_VERSION 1
+
+typedef enum {
+  MOESQ_OK = 0,
+  MOESQ_ERR_INVALID = -1,      /* a null pointer, a negative or inconsistent size, a bad enum */
+  MOESQ_ERR_UNSUPPORTED = -2,  /* valid but outside what the kernels handle (a K not multiple of 256 ...) */
+  MOESQ_ERR_WORKSPACE = -3,    /* workspace smaller than the size query returns */
+  MOESQ_ERR_HIP = -4           /* a HIP launch or synchronization failed; see moesq_last_error() */
+} moesq_status;
+
+typedef enum { MOESQ_BF16 = 0, MOESQ_F32 = 1 } moesq_dtype;
+
+/* moe_ffn flags */
+#define MOESQ_FLAG_SYNC_CHECK 1u    /* synchronize the stream before returning and report kernel errors */
+
+/* Weights of one linear of every expert, in pair-bitmask storage. Host struct, read during the call
+ * only; its pointers are device memory. Expert e's tensors start at e * N * (K/4), e * N * (K/16),
+ * e * N * (K/32) and e * G. G = 2 for a fused gate|up linear: rows [0, N/2) are gate_proj and take
+ * global[e*2 + 0], rows [N/2, N) are up_proj and take global[e*2 + 1] (gate and up carry separate
+ * global scales: model cards "Qwen3.8-Flash-Next-P48NVFP4-MoESQ" and "Qwen3-30B-A3B-P48NVFP4-MoESQ");
+ * G = 1 otherwise. Every pointer 16-byte aligned. */
+typedef struct {
+  const uint8_t *packed;   /* [E][N][K/4]  */
+  const uint8_t *mask;     /* [E][N][K/16] */
+  const uint8_t *scale;    /* [E][N][K/32] */
+  const float *global;     /* [E][G]       */
+  int32_t E, N, K, G;
+} moesq_weights;
+
+int moesq_abi_version(void);
+const char *moesq_status_string(moesq_status s);           /* static string, host */
+const char *moesq_last_error(void);                         /* thread-local text of the last failure, host */
+
+/* NVFP4 quantization of activation rows (model card "Compression details", Activations row).
+ *   x        [*][x_row_stride] bf16 or fp32 values; row r of the output reads x row src_row[r]
+ *            (src_row NULL: row r).
+ *   rows, K  output rows and K (K % 32 == 0; rows >= 0).
+ *   expert_offsets [E+1] (optional): row r uses global[e] for offsets[e] <= r < offsets[e+1]; rows
+ *            outside [offsets[0], offsets[E]) are not written. NULL: every row uses global[0].
+ *   global   activation global scale(s) > 0 (finite, >= 2^-90 for exact rounding decisions).
+ *   codes    [rows][K/2] out: two E2M1 codes per byte, lower K in the low nibble.
+ *   scales   [rows][K/32] out: E4M3 bytes. x must be 16-byte aligned per row group. */
+moesq_status moesq_quantize_act(const void *x, moesq_dtype x_dtype, int64_t rows, int32_t K,
+                                int64_t x_row_stride, const int32_t *src_row,
+                                const int32_t *expert_offsets, int32_t E, const float *global,
+                                uint8_t *codes, uint8_t *scales, hipStream_t stream);
+
+/* Stable grouping of the router's (token, slot) pairs p = t*k + j by expert id (the grouped GEMM runs
+ * one GEMM per expert over its rows).
+ *   topk_ids [T][k] int32 in [0, E), or -1 to drop the pair (ids outside [-1, E) are also dropped and
+ *            counted in *status).
+ *   counts [E], offsets [E+1] (exclusive prefix of counts), sorted [T*k] (the offsets[E] live pair ids
+ *   in (expert, p) order; the tail is not written), inv [T*k] (row of pair p, -1 if dropped),
+ *   status [1] int32 (count of ids outside [-1, E)). E in [1, 1024], k in [1, 32]. */
+moesq_status moesq_permute(const int32_t *topk_ids, int64_t T, int32_t k, int32_t E, int32_t *counts,
+                           int32_t *offsets, int32_t *sorted, int32_t *inv, int32_t *status,
+                           hipStream_t stream);
+
+/* Grouped sparse GEMM (model card "Qwen3.5-397B-A17B-P48NVFP4-MoESQ": paired-4:8 sparse NVFP4
+ * grouped GEMM over the routed experts): for each expert e and row r in [offsets[e], offsets[e+1]):
+ *   out[r][n] = a_global[e] * wglobal(e, n) * sum_K e2m1(a)e4m3(a_scale) * e2m1(w)e4m3(w_scale)
+ *   a_codes [rows][K/2], a_scales [rows][K/32] (as moesq_quantize_act writes them), a_global [E],
+ *   expert_offsets [E+1] with offsets[E] <= rows, w: K % 256 == 0, N % 64 == 0, G in {1, 2}.
+ *   out [rows][N] fp32: rows of an expert are overwritten, other rows are not written.
+ *   workspace: moesq_grouped_gemm_workspace_size(E) bytes of device scratch. */
+size_t moesq_grouped_gemm_workspace_size(int32_t E);
+moesq_status moesq_grouped_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_global,
+                                const int32_t *expert_offsets, int64_t rows, const moesq_weights *w,
+                                float *out, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* MoE FFN of T tokens through the routed experts (the W4A4 paired-4:8 expert path):
+ *   for each pair (t, j) with e = topk_ids[t][j] >= 0:
+ *     a13 = NVFP4(x[t], a13_global[e]);  [gate | up] = a13 @ W13_e^T;  h = silu(gate) * up
+ *     a2  = NVFP4(h, a2_global[e]);      y = a2 @ W2_e^T
+ *     out[t] += topk_weights[t][j] * y          (sum over j in j order, fp32)
+ *   x [T][H] bf16; topk_ids, topk_weights [T][k]; w13: N = 2I, K = H, G = 2; w2: N = H, K = I, G = 1;
+ *   silu(v) = v / (1 + exp(-v)); h is kept in fp32 before its quantization.
+ *   out [T][H] fp32, overwritten. H % 256 == 0, I % 256 == 0.
+ *   workspace: moesq_moe_ffn_workspace_size(...) bytes. After the call (stream order) it holds the
+ *   intermediates at the offsets moesq_moe_ffn_layout() reports: counts, offsets, sorted, inv, the
+ *   gate/up input codes+scales a13 and the down input codes+scales a2 (rows in sorted order), and the
+ *   per-row down outputs (already times the router weight). */
+typedef struct {
+  size_t counts, offsets, tile_offsets, sorted, inv, status;
+  size_t a13_codes, a13_scales, a2_codes, a2_scales, down_rows;
+  size_t total;
+  int32_t rows_per_mblock;   /* m-block size of the tactic the call uses */
+} moesq_ffn_layout;
+moesq_status moesq_moe_ffn_layout(int64_t T, int32_t H, int32_t I, int32_t k, int32_t E, uint32_t flags,
+                                  moesq_ffn_layout *layout /* host */);
+size_t moesq_moe_ffn_workspace_size(int64_t T, int32_t H, int32_t I, int32_t k, int32_t E, uint32_t flags);
+moesq_status moesq_moe_ffn(const void *x, int64_t T, int32_t H, const int32_t *topk_ids,
+                           const float *topk_weights, int32_t k, const moesq_weights *w13,
+                           const moesq_weights *w2, const float *a13_global, const float *a2_global,
+                           float *out, void *workspace, size_t workspace_bytes, uint32_t flags,
+                           hipStream_t stream);
+
+/* Weight compression of a dense fp32 linear [N][K] into pair-bitmask NVFP4 (the synthetic-layer
+ * recipe; model card "Compression details": paired 4:8 along K, 2 of every 4 pairs kept): in each
+ * 8-K chunk keep the 2 pairs with the largest a*a + b*b (float64, ties to the lower pair),
+ * global = fp32(amax of kept values) / 2688, then the NVFP4 rule above; pruned pairs are byte 0x00
+ * and the mask names the kept pairs. global: 1 float out. K % 32 == 0. */
+moesq_status moesq_compress_weights(const float *w, int64_t N, int32_t K, uint8_t *packed, uint8_t *mask,
+                                    uint8_t *scale, float *global, hipStream_t stream);
+
+/* Storage codec on whole tensors of `rows` rows of K (model card "Sparse storage layout": the encoding
+ * is lossless).
+ *   validate: *bad = number of chunk nibbles without exactly two bits set.
+ *   unpack:   sparse -> dense packed NVFP4 [rows][K/2] (pruned bytes 0x00); a bad nibble is counted
+ *             in *bad and its chunk written as zeros.
+ *   pack:     dense -> sparse with the kept bytes = the nonzero ones, a chunk with fewer than two
+ *             completed with its lowest-index zero bytes; a chunk with more than two is counted in
+ *             *bad. K % 16 == 0 (K % 32 for whole mask bytes per row). bad: 1 int32. */
+moesq_status moesq_validate_weights(const uint8_t *mask, int64_t rows, int32_t K, int32_t *bad,
+                                    hipStream_t stream);
+moesq_status moesq_unpack_pair_bitmask(const uint8_t *packed, const uint8_t *mask, int64_t rows, int32_t K,
+                                       uint8_t *dense, int32_t *bad, hipStream_t stream);
+moesq_status moesq_pack_pair_bitmask(const uint8_t *dense, int64_t rows, int32_t K, uint8_t *packed,
+                                     uint8_t *mask, int32_t *bad, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOESQ_H_ */

@@ -1,0 +1,315 @@
+"""moesq: paired-4:8 sparse NVFP4 (W4A4) MoE expert path for AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding of the in-tree HIP library ``libmoesq.so`` (C ABI in ``include/moesq.h``). It only
+marshals arguments: every step runs in the library's kernels on the tensors' device, on torch's
+current stream. There is no CPU fallback: a missing library or a CPU tensor raises ``MoesqError``.
+
+Weights use the pair-bitmask storage of the MoESQ model cards ("Sparse storage layout"): per expert
+linear ``packed`` u8 [N, K/4], ``mask`` u8 [N, K/16], ``scale`` u8 (E4M3 bits) [N, K/32] and an fp32
+global per tensor (two, gate and up, for a fused gate|up linear).
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "MoesqError", "SparseWeights", "lib", "library_path", "abi_version", "quantize_act", "permute",
+    "grouped_gemm", "moe_ffn", "ffn_layout", "compress_weights", "compress_moe_layer", "validate_weights",
+    "pack_pair_bitmask", "unpack_pair_bitmask", "FLAG_SYNC_CHECK", "EXPORTED_SYMBOLS",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_PKG, "libmoesq.so")
+FLAG_SYNC_CHECK = 1
+
+#: Every function the C ABI exports (include/moesq.h).
+EXPORTED_SYMBOLS = (
+    "moesq_abi_version", "moesq_status_string", "moesq_last_error", "moesq_quantize_act", "moesq_permute",
+    "moesq_grouped_gemm_workspace_size", "moesq_grouped_gemm", "moesq_moe_ffn_layout",
+    "moesq_moe_ffn_workspace_size", "moesq_moe_ffn", "moesq_compress_weights", "moesq_validate_weights",
+    "moesq_unpack_pair_bitmask", "moesq_pack_pair_bitmask",
+)
+
+
+class MoesqError(RuntimeError):
+    pass
+
+
+class _CWeights(ctypes.Structure):
+    _fields_ = [("packed", ctypes.c_void_p), ("mask", ctypes.c_void_p), ("scale", ctypes.c_void_p),
+                ("global_", ctypes.c_void_p), ("E", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("K", ctypes.c_int32), ("G", ctypes.c_int32)]
+
+
+class _CLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in ("counts", "offsets", "tile_offsets", "sorted", "inv", "status",
+                                                "a13_codes", "a13_scales", "a2_codes", "a2_scales",
+                                                "down_rows", "total")] + [("rows_per_mblock", ctypes.c_int32)]
+
+
+_lib: Optional[ctypes.CDLL] = None
+_P, _I32, _I64, _SZ, _U32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_uint32
+
+
+def _declare(L: ctypes.CDLL) -> None:
+    sig = {
+        "moesq_abi_version": (ctypes.c_int, []),
+        "moesq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "moesq_last_error": (ctypes.c_char_p, []),
+        "moesq_quantize_act": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I32, _I64, _P, _P, _I32, _P, _P, _P, _P]),
+        "moesq_permute": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P]),
+        "moesq_grouped_gemm_workspace_size": (_SZ, [_I32]),
+        "moesq_grouped_gemm": (ctypes.c_int, [_P, _P, _P, _P, _I64, ctypes.POINTER(_CWeights), _P, _P, _SZ, _P]),
+        "moesq_moe_ffn_layout": (ctypes.c_int, [_I64, _I32, _I32, _I32, _I32, _U32, ctypes.POINTER(_CLayout)]),
+        "moesq_moe_ffn_workspace_size": (_SZ, [_I64, _I32, _I32, _I32, _I32, _U32]),
+        "moesq_moe_ffn": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _I32, ctypes.POINTER(_CWeights),
+                                         ctypes.POINTER(_CWeights), _P, _P, _P, _P, _SZ, _U32, _P]),
+        "moesq_compress_weights": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _P, _P, _P]),
+        "moesq_validate_weights": (ctypes.c_int, [_P, _I64, _I32, _P, _P]),
+        "moesq_unpack_pair_bitmask": (ctypes.c_int, [_P, _P, _I64, _I32, _P, _P, _P]),
+        "moesq_pack_pair_bitmask": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _P, _P]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise MoesqError(f"{library_path} is missing: build it with `python -m sparse_quantized_moe_amd.build`")
+        L = ctypes.CDLL(library_path)
+        _declare(L)
+        _lib = L
+    return _lib
+
+
+def abi_version() -> int:
+    return lib().moesq_abi_version()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        L = lib()
+        raise MoesqError(f"{L.moesq_status_string(status).decode()}: {L.moesq_last_error().decode()}")
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise MoesqError(f"{name} must be a GPU tensor (the library has no CPU path)")
+    if dtype is not None and t.dtype != dtype:
+        raise MoesqError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise MoesqError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+@dataclasses.dataclass
+class SparseWeights:
+    """One linear of every expert in pair-bitmask storage (device tensors)."""
+    packed: torch.Tensor        # uint8 [E, N, K/4]
+    mask: torch.Tensor          # uint8 [E, N, K/16]
+    scale: torch.Tensor         # uint8 [E, N, K/32]   (E4M3 bits)
+    global_scale: torch.Tensor  # float32 [E, G]
+
+    @property
+    def E(self) -> int:
+        return self.packed.shape[0]
+
+    @property
+    def N(self) -> int:
+        return self.packed.shape[1]
+
+    @property
+    def K(self) -> int:
+        return self.packed.shape[2] * 4
+
+    @property
+    def G(self) -> int:
+        return self.global_scale.shape[1]
+
+    def c_struct(self) -> _CWeights:
+        E, N, K = self.E, self.N, self.K
+        if tuple(self.mask.shape) != (E, N, K // 16) or tuple(self.scale.shape) != (E, N, K // 32):
+            raise MoesqError("mask/scale shapes do not match packed")
+        return _CWeights(_dev(self.packed, "packed", torch.uint8), _dev(self.mask, "mask", torch.uint8),
+                         _dev(self.scale, "scale", torch.uint8),
+                         _dev(self.global_scale, "global_scale", torch.float32), E, N, K, self.G)
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in (self.packed, self.mask, self.scale, self.global_scale))
+
+
+def quantize_act(x: torch.Tensor, global_scale: torch.Tensor, src_row: Optional[torch.Tensor] = None,
+                 expert_offsets: Optional[torch.Tensor] = None, rows: Optional[int] = None):
+    """NVFP4 codes [rows, K/2] and E4M3 scales [rows, K/32] of the rows of x (bf16 or fp32 [*, K])."""
+    if x.dtype not in (torch.bfloat16, torch.float32) or x.dim() != 2:
+        raise MoesqError("x must be a 2-D bf16 or fp32 tensor")
+    K = x.shape[1]
+    rows = (src_row.shape[0] if src_row is not None else x.shape[0]) if rows is None else rows
+    codes = torch.empty((rows, K // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((rows, K // 32), dtype=torch.uint8, device=x.device)
+    E = 0 if expert_offsets is None else expert_offsets.shape[0] - 1
+    _check(lib().moesq_quantize_act(
+        _dev(x, "x"), 1 if x.dtype == torch.float32 else 0, rows, K, x.stride(0),
+        None if src_row is None else _dev(src_row, "src_row", torch.int32),
+        None if expert_offsets is None else _dev(expert_offsets, "expert_offsets", torch.int32), E,
+        _dev(global_scale, "global_scale", torch.float32), _dev(codes, "codes"), _dev(scales, "scales"), _stream()))
+    return codes, scales
+
+
+def permute(topk_ids: torch.Tensor, E: int):
+    """(counts [E], offsets [E+1], sorted [T*k], inv [T*k], status [1]) int32 of the stable grouping."""
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    sorted_ = torch.full((T * k,), -1, dtype=torch.int32, device=dev)
+    inv = torch.empty(T * k, dtype=torch.int32, device=dev)
+    status = torch.empty(1, dtype=torch.int32, device=dev)
+    _check(lib().moesq_permute(_dev(topk_ids, "topk_ids", torch.int32), T, k, E, _dev(counts, "counts"),
+                               _dev(offsets, "offsets"), _dev(sorted_, "sorted"), _dev(inv, "inv"),
+                               _dev(status, "status"), _stream()))
+    return counts, offsets, sorted_, inv, status
+
+
+def grouped_gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, a_global: torch.Tensor,
+                 expert_offsets: torch.Tensor, w: SparseWeights, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp32 [rows, N]: each expert's rows of the NVFP4 activations times its sparse weight."""
+    rows = a_codes.shape[0]
+    if out is None:
+        out = torch.zeros((rows, w.N), dtype=torch.float32, device=a_codes.device)
+    ws_bytes = lib().moesq_grouped_gemm_workspace_size(w.E)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=a_codes.device)
+    cw = w.c_struct()
+    _check(lib().moesq_grouped_gemm(_dev(a_codes, "a_codes", torch.uint8), _dev(a_scales, "a_scales", torch.uint8),
+                                    _dev(a_global, "a_global", torch.float32),
+                                    _dev(expert_offsets, "expert_offsets", torch.int32), rows, ctypes.byref(cw),
+                                    _dev(out, "out", torch.float32), _dev(ws, "workspace"), ws_bytes, _stream()))
+    return out
+
+
+def ffn_layout(T: int, H: int, I: int, k: int, E: int, flags: int = 0) -> dict:
+    L = _CLayout()
+    _check(lib().moesq_moe_ffn_layout(T, H, I, k, E, flags, ctypes.byref(L)))
+    return {n: getattr(L, n) for n, _ in _CLayout._fields_}
+
+
+def moe_ffn(x: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.Tensor, w13: SparseWeights,
+            w2: SparseWeights, a13_global: torch.Tensor, a2_global: torch.Tensor, out: Optional[torch.Tensor] = None,
+            workspace: Optional[torch.Tensor] = None, flags: int = 0) -> torch.Tensor:
+    """fp32 [T, H] MoE FFN output of bf16 tokens x [T, H] (see moesq_moe_ffn)."""
+    T, H = x.shape
+    k = topk_ids.shape[1]
+    I = w2.K
+    ws_bytes = lib().moesq_moe_ffn_workspace_size(T, H, I, k, w13.E, flags)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float32, device=x.device)
+    c13, c2 = w13.c_struct(), w2.c_struct()
+    _check(lib().moesq_moe_ffn(_dev(x, "x", torch.bfloat16), T, H, _dev(topk_ids, "topk_ids", torch.int32),
+                               _dev(topk_weights, "topk_weights", torch.float32), k, ctypes.byref(c13),
+                               ctypes.byref(c2), _dev(a13_global, "a13_global", torch.float32),
+                               _dev(a2_global, "a2_global", torch.float32), _dev(out, "out", torch.float32),
+                               _dev(workspace, "workspace"), workspace.numel(), flags, _stream()))
+    return out
+
+
+def ffn_intermediates(workspace: torch.Tensor, T: int, H: int, I: int, k: int, E: int) -> dict:
+    """Views of the intermediates a moe_ffn call left in its workspace (stream-ordered after the call)."""
+    L = ffn_layout(T, H, I, k, E)
+    P = T * k
+
+    def view(off, n, dtype, shape):
+        b = workspace[off: off + n * torch.tensor([], dtype=dtype).element_size()]
+        return b.view(dtype).view(shape)
+    return {
+        "counts": view(L["counts"], E, torch.int32, (E,)),
+        "offsets": view(L["offsets"], E + 1, torch.int32, (E + 1,)),
+        "sorted": view(L["sorted"], P, torch.int32, (P,)),
+        "inv": view(L["inv"], P, torch.int32, (P,)),
+        "status": view(L["status"], 1, torch.int32, (1,)),
+        "a13_codes": view(L["a13_codes"], P * H // 2, torch.uint8, (P, H // 2)),
+        "a13_scales": view(L["a13_scales"], P * H // 32, torch.uint8, (P, H // 32)),
+        "a2_codes": view(L["a2_codes"], P * I // 2, torch.uint8, (P, I // 2)),
+        "a2_scales": view(L["a2_scales"], P * I // 32, torch.uint8, (P, I // 32)),
+        "down_rows": view(L["down_rows"], P * H, torch.float32, (P, H)),
+    }
+
+
+__all__.append("ffn_intermediates")
+
+
+def compress_weights(w: torch.Tensor, packed: Optional[torch.Tensor] = None, mask: Optional[torch.Tensor] = None,
+                     scale: Optional[torch.Tensor] = None, global_out: Optional[torch.Tensor] = None):
+    """Dense fp32 [N, K] -> (packed [N,K/4], mask [N,K/16], scale [N,K/32], global [1]) pair-bitmask NVFP4."""
+    N, K = w.shape
+    dev = w.device
+    packed = torch.empty((N, K // 4), dtype=torch.uint8, device=dev) if packed is None else packed
+    mask = torch.empty((N, K // 16), dtype=torch.uint8, device=dev) if mask is None else mask
+    scale = torch.empty((N, K // 32), dtype=torch.uint8, device=dev) if scale is None else scale
+    global_out = torch.empty(1, dtype=torch.float32, device=dev) if global_out is None else global_out
+    _check(lib().moesq_compress_weights(_dev(w, "w", torch.float32), N, K, _dev(packed, "packed"), _dev(mask, "mask"),
+                                        _dev(scale, "scale"), _dev(global_out, "global"), _stream()))
+    return packed, mask, scale, global_out
+
+
+def compress_moe_layer(E: int, H: int, I: int, dense_expert, device="cuda"):
+    """Pair-bitmask storage of a whole MoE layer from ``dense_expert(e) -> (gate [I,H], up [I,H], down [H,I])``
+    fp32 device tensors: returns (w13 with rows [gate; up] and G = 2, w2 with G = 1)."""
+    w13 = SparseWeights(torch.empty((E, 2 * I, H // 4), dtype=torch.uint8, device=device),
+                        torch.empty((E, 2 * I, H // 16), dtype=torch.uint8, device=device),
+                        torch.empty((E, 2 * I, H // 32), dtype=torch.uint8, device=device),
+                        torch.empty((E, 2), dtype=torch.float32, device=device))
+    w2 = SparseWeights(torch.empty((E, H, I // 4), dtype=torch.uint8, device=device),
+                       torch.empty((E, H, I // 16), dtype=torch.uint8, device=device),
+                       torch.empty((E, H, I // 32), dtype=torch.uint8, device=device),
+                       torch.empty((E, 1), dtype=torch.float32, device=device))
+    for e in range(E):
+        g, u, d = dense_expert(e)
+        compress_weights(g.contiguous(), w13.packed[e, :I], w13.mask[e, :I], w13.scale[e, :I], w13.global_scale[e, 0:1])
+        compress_weights(u.contiguous(), w13.packed[e, I:], w13.mask[e, I:], w13.scale[e, I:], w13.global_scale[e, 1:2])
+        compress_weights(d.contiguous(), w2.packed[e], w2.mask[e], w2.scale[e], w2.global_scale[e, 0:1])
+    return w13, w2
+
+
+def validate_weights(mask: torch.Tensor, K: int) -> int:
+    """Number of chunk masks without exactly two bits set (synchronizes)."""
+    rows = mask.numel() // (K // 16)
+    bad = torch.empty(1, dtype=torch.int32, device=mask.device)
+    _check(lib().moesq_validate_weights(_dev(mask, "mask", torch.uint8), rows, K, _dev(bad, "bad"), _stream()))
+    return int(bad.item())
+
+
+def unpack_pair_bitmask(packed: torch.Tensor, mask: torch.Tensor, K: int):
+    """Sparse -> dense packed NVFP4 [rows, K/2]; returns (dense, bad-count tensor)."""
+    rows = packed.numel() // (K // 4)
+    dense = torch.empty((rows, K // 2), dtype=torch.uint8, device=packed.device)
+    bad = torch.empty(1, dtype=torch.int32, device=packed.device)
+    _check(lib().moesq_unpack_pair_bitmask(_dev(packed, "packed", torch.uint8), _dev(mask, "mask", torch.uint8), rows, K,
+                                           _dev(dense, "dense"), _dev(bad, "bad"), _stream()))
+    return dense, bad
+
+
+def pack_pair_bitmask(dense: torch.Tensor, K: int):
+    """Dense packed NVFP4 [rows, K/2] -> (packed [rows, K/4], mask [rows, K/16], bad-count tensor)."""
+    rows = dense.numel() // (K // 2)
+    packed = torch.empty((rows, K // 4), dtype=torch.uint8, device=dense.device)
+    mask = torch.empty((rows, K // 16), dtype=torch.uint8, device=dense.device)
+    bad = torch.empty(1, dtype=torch.int32, device=dense.device)
+    _check(lib().moesq_pack_pair_bitmask(_dev(dense, "dense", torch.uint8), rows, K, _dev(packed, "packed"),
+                                         _dev(mask, "mask"), _dev(bad, "bad"), _stream()))
+    return packed, mask, bad

@@ -1,0 +1,248 @@
+// C ABI of the moesq library: argument checks, workspace layout and kernel launches.
+#include <string>
+#include <cstdio>
+
+#include "../../include/moesq.h"
+#include "moesq_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moesq_status fail(moesq_status s, const char* fmt, const char* what) {
+  char buf[512];
+  std::snprintf(buf, sizeof buf, fmt, what);
+  g_last_error = buf;
+  return s;
+}
+#define MOESQ_REQUIRE(cond, status, msg) \
+  do { if (!(cond)) return fail(status, "%s", msg); } while (0)
+
+moesq_status check_launch(hipStream_t stream, bool sync) {
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && sync) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(MOESQ_ERR_HIP, "HIP error: %s", hipGetErrorString(e));
+  return MOESQ_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+moesq_status check_weights(const moesq_weights* w, const char* name) {
+  if (!w) return fail(MOESQ_ERR_INVALID, "%s: null weights struct", name);
+  if (!w->packed || !w->mask || !w->scale || !w->global) return fail(MOESQ_ERR_INVALID, "%s: null weight pointer", name);
+  if (w->E < 1 || w->N < 1 || w->K < 1) return fail(MOESQ_ERR_INVALID, "%s: E, N, K must be positive", name);
+  if (w->G != 1 && w->G != 2) return fail(MOESQ_ERR_INVALID, "%s: G must be 1 or 2", name);
+  if (w->K % 32) return fail(MOESQ_ERR_INVALID, "%s: K must be a multiple of 32", name);
+  if (w->K % 256) return fail(MOESQ_ERR_UNSUPPORTED, "%s: the GEMM needs K % 256 == 0", name);
+  if (w->N % 64) return fail(MOESQ_ERR_UNSUPPORTED, "%s: the GEMM needs N % 64 == 0", name);
+  if (w->E > 1024) return fail(MOESQ_ERR_UNSUPPORTED, "%s: at most 1024 experts", name);
+  if (!aligned16(w->packed) || !aligned16(w->mask) || !aligned16(w->scale))
+    return fail(MOESQ_ERR_INVALID, "%s: weight tensors must be 16-byte aligned", name);
+  return MOESQ_OK;
+}
+
+int ffn_tactic(int64_t T, int32_t k, int32_t E) {
+  // mean rows per expert: small batches stream each expert once, large ones reuse weight fragments
+  return (T * k) <= (int64_t)48 * E ? moesq::kTacticDecode : moesq::kTacticPrefill;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moesq_abi_version(void) { return MOESQ_ABI_VERSION; }
+
+const char* moesq_status_string(moesq_status s) {
+  switch (s) {
+    case MOESQ_OK: return "ok";
+    case MOESQ_ERR_INVALID: return "invalid argument";
+    case MOESQ_ERR_UNSUPPORTED: return "unsupported shape";
+    case MOESQ_ERR_WORKSPACE: return "workspace too small";
+    case MOESQ_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* moesq_last_error(void) { return g_last_error.c_str(); }
+
+moesq_status moesq_quantize_act(const void* x, moesq_dtype x_dtype, int64_t rows, int32_t K, int64_t x_row_stride,
+                                const int32_t* src_row, const int32_t* expert_offsets, int32_t E, const float* global,
+                                uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+  MOESQ_REQUIRE(rows >= 0 && K > 0, MOESQ_ERR_INVALID, "quantize_act: rows >= 0 and K > 0 required");
+  MOESQ_REQUIRE(K % 32 == 0, MOESQ_ERR_INVALID, "quantize_act: K must be a multiple of 32");
+  MOESQ_REQUIRE(x_dtype == MOESQ_BF16 || x_dtype == MOESQ_F32, MOESQ_ERR_INVALID, "quantize_act: bad dtype");
+  if (rows == 0) return MOESQ_OK;
+  MOESQ_REQUIRE(x && global && codes && scales, MOESQ_ERR_INVALID, "quantize_act: null pointer");
+  MOESQ_REQUIRE(x_row_stride >= K, MOESQ_ERR_INVALID, "quantize_act: x_row_stride < K");
+  MOESQ_REQUIRE(aligned16(x) && aligned16(codes), MOESQ_ERR_INVALID, "quantize_act: x and codes must be 16-byte aligned");
+  MOESQ_REQUIRE((x_row_stride * (x_dtype == MOESQ_F32 ? 4 : 2)) % 16 == 0, MOESQ_ERR_INVALID,
+                "quantize_act: x row stride must be a multiple of 16 bytes");
+  MOESQ_REQUIRE(!expert_offsets || E >= 1, MOESQ_ERR_INVALID, "quantize_act: E >= 1 with expert_offsets");
+  moesq::launch_quantize(x, x_dtype == MOESQ_F32, rows, K, x_row_stride, src_row, expert_offsets, E, nullptr,
+                         nullptr, nullptr, 1, global, codes, scales,
+                         expert_offsets ? moesq::kQuantOffsets : moesq::kQuantSingle, stream);
+  return check_launch(stream, false);
+}
+
+moesq_status moesq_permute(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E, int32_t* counts, int32_t* offsets,
+                           int32_t* sorted, int32_t* inv, int32_t* status, hipStream_t stream) {
+  MOESQ_REQUIRE(T >= 0 && k >= 1 && k <= 32 && E >= 1, MOESQ_ERR_INVALID, "permute: T >= 0, 1 <= k <= 32, E >= 1");
+  MOESQ_REQUIRE(E <= 1024, MOESQ_ERR_UNSUPPORTED, "permute: at most 1024 experts");
+  MOESQ_REQUIRE(counts && offsets && status && (T == 0 || (topk_ids && sorted && inv)), MOESQ_ERR_INVALID,
+                "permute: null pointer");
+  MOESQ_REQUIRE(T * k < (int64_t)1 << 31, MOESQ_ERR_UNSUPPORTED, "permute: T*k must fit in int32");
+  moesq::launch_permute(topk_ids, T, k, E, counts, offsets, sorted, inv, nullptr, 0, status, stream);
+  return check_launch(stream, false);
+}
+
+size_t moesq_grouped_gemm_workspace_size(int32_t E) { return align256((size_t)(E + 1) * 4); }
+
+moesq_status moesq_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global,
+                                const int32_t* expert_offsets, int64_t rows, const moesq_weights* w, float* out,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  moesq_status s = check_weights(w, "grouped_gemm");
+  if (s != MOESQ_OK) return s;
+  MOESQ_REQUIRE(rows >= 0, MOESQ_ERR_INVALID, "grouped_gemm: rows >= 0");
+  if (rows == 0) return MOESQ_OK;
+  MOESQ_REQUIRE(a_codes && a_scales && a_global && expert_offsets && out && workspace, MOESQ_ERR_INVALID,
+                "grouped_gemm: null pointer");
+  MOESQ_REQUIRE(workspace_bytes >= moesq_grouped_gemm_workspace_size(w->E), MOESQ_ERR_WORKSPACE,
+                "grouped_gemm: workspace too small");
+  MOESQ_REQUIRE(aligned16(out) && aligned16(a_codes), MOESQ_ERR_INVALID, "grouped_gemm: out and a_codes must be 16-byte aligned");
+  MOESQ_REQUIRE(rows * w->K / 2 < ((int64_t)1 << 40), MOESQ_ERR_UNSUPPORTED, "grouped_gemm: too many rows");
+  const int tactic = ffn_tactic(rows, 1, w->E);
+  int32_t* tile_offsets = static_cast<int32_t*>(workspace);
+  moesq::launch_tile_offsets(expert_offsets, w->E, moesq::tactic_rows_per_mblock(tactic), tile_offsets, stream);
+  moesq::GemmParams p{};
+  p.a_codes = a_codes; p.a_scales = a_scales; p.a_global = a_global; p.offsets = expert_offsets;
+  p.tile_offsets = tile_offsets; p.rows = rows;
+  p.w_packed = w->packed; p.w_mask = w->mask; p.w_scale = w->scale; p.w_global = w->global;
+  p.E = w->E; p.N = w->N; p.K = w->K; p.G = w->G; p.out = out;
+  moesq::launch_grouped_gemm(p, moesq::kEpiStore, tactic, stream);
+  return check_launch(stream, false);
+}
+
+moesq_status moesq_moe_ffn_layout(int64_t T, int32_t H, int32_t I, int32_t k, int32_t E, uint32_t flags,
+                                  moesq_ffn_layout* L) {
+  (void)flags;
+  MOESQ_REQUIRE(L, MOESQ_ERR_INVALID, "moe_ffn_layout: null layout");
+  MOESQ_REQUIRE(T >= 0 && H > 0 && I > 0 && k >= 1 && E >= 1, MOESQ_ERR_INVALID, "moe_ffn_layout: bad sizes");
+  const size_t P = (size_t)T * k;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+  L->counts = take((size_t)E * 4);
+  L->offsets = take((size_t)(E + 1) * 4);
+  L->tile_offsets = take((size_t)(E + 1) * 4);
+  L->status = take(4);
+  L->sorted = take(P * 4);
+  L->inv = take(P * 4);
+  L->a13_codes = take(P * (size_t)(H / 2));
+  L->a13_scales = take(P * (size_t)(H / 32));
+  L->a2_codes = take(P * (size_t)(I / 2));
+  L->a2_scales = take(P * (size_t)(I / 32));
+  L->down_rows = take(P * (size_t)H * 4);
+  L->total = off;
+  L->rows_per_mblock = moesq::tactic_rows_per_mblock(ffn_tactic(T, k, E));
+  return MOESQ_OK;
+}
+
+size_t moesq_moe_ffn_workspace_size(int64_t T, int32_t H, int32_t I, int32_t k, int32_t E, uint32_t flags) {
+  moesq_ffn_layout L;
+  if (moesq_moe_ffn_layout(T, H, I, k, E, flags, &L) != MOESQ_OK) return 0;
+  return L.total;
+}
+
+moesq_status moesq_moe_ffn(const void* x, int64_t T, int32_t H, const int32_t* topk_ids, const float* topk_weights,
+                           int32_t k, const moesq_weights* w13, const moesq_weights* w2, const float* a13_global,
+                           const float* a2_global, float* out, void* workspace, size_t workspace_bytes, uint32_t flags,
+                           hipStream_t stream) {
+  moesq_status s = check_weights(w13, "moe_ffn w13");
+  if (s != MOESQ_OK) return s;
+  s = check_weights(w2, "moe_ffn w2");
+  if (s != MOESQ_OK) return s;
+  MOESQ_REQUIRE(T >= 0 && k >= 1 && k <= 32, MOESQ_ERR_INVALID, "moe_ffn: T >= 0 and 1 <= k <= 32");
+  const int32_t E = w13->E, I = w2->K;
+  MOESQ_REQUIRE(w2->E == E, MOESQ_ERR_INVALID, "moe_ffn: w13 and w2 expert counts differ");
+  MOESQ_REQUIRE(w13->G == 2 && w2->G == 1, MOESQ_ERR_INVALID, "moe_ffn: w13 needs G = 2 (gate|up), w2 G = 1");
+  MOESQ_REQUIRE(w13->K == H && w2->N == H && w13->N == 2 * I, MOESQ_ERR_INVALID,
+                "moe_ffn: shapes must be w13 [2I, H], w2 [H, I]");
+  MOESQ_REQUIRE(I % 256 == 0 && H % 256 == 0, MOESQ_ERR_UNSUPPORTED, "moe_ffn: H and I must be multiples of 256");
+  MOESQ_REQUIRE(T * k < ((int64_t)1 << 31), MOESQ_ERR_UNSUPPORTED, "moe_ffn: T*k must fit in int32");
+  if (T == 0) return MOESQ_OK;
+  MOESQ_REQUIRE(x && topk_ids && topk_weights && a13_global && a2_global && out && workspace, MOESQ_ERR_INVALID,
+                "moe_ffn: null pointer");
+  MOESQ_REQUIRE(aligned16(x) && aligned16(out) && aligned16(workspace), MOESQ_ERR_INVALID,
+                "moe_ffn: x, out and workspace must be 16-byte aligned");
+  moesq_ffn_layout L;
+  moesq_moe_ffn_layout(T, H, I, k, E, flags, &L);
+  MOESQ_REQUIRE(workspace_bytes >= L.total, MOESQ_ERR_WORKSPACE, "moe_ffn: workspace too small");
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  int32_t* tile_offsets = reinterpret_cast<int32_t*>(ws + L.tile_offsets);
+  int32_t* status = reinterpret_cast<int32_t*>(ws + L.status);
+  int32_t* sorted = reinterpret_cast<int32_t*>(ws + L.sorted);
+  int32_t* inv = reinterpret_cast<int32_t*>(ws + L.inv);
+  uint8_t* a13c = ws + L.a13_codes;
+  uint8_t* a13s = ws + L.a13_scales;
+  uint8_t* a2c = ws + L.a2_codes;
+  uint8_t* a2s = ws + L.a2_scales;
+  float* drows = reinterpret_cast<float*>(ws + L.down_rows);
+  const int tactic = ffn_tactic(T, k, E);
+  const int64_t P = T * k;
+
+  moesq::launch_permute(topk_ids, T, k, E, counts, offsets, sorted, inv, tile_offsets, L.rows_per_mblock, status, stream);
+  moesq::launch_quantize(x, false, P, H, H, nullptr, nullptr, E, sorted, topk_ids, offsets + E, k, a13_global, a13c,
+                         a13s, moesq::kQuantPairs, stream);
+  moesq::GemmParams g{};
+  g.a_codes = a13c; g.a_scales = a13s; g.a_global = a13_global; g.offsets = offsets; g.tile_offsets = tile_offsets;
+  g.rows = P; g.w_packed = w13->packed; g.w_mask = w13->mask; g.w_scale = w13->scale; g.w_global = w13->global;
+  g.E = E; g.N = w13->N; g.K = H; g.G = 2; g.h_codes = a2c; g.h_scales = a2s; g.h_global = a2_global;
+  moesq::launch_grouped_gemm(g, moesq::kEpiGateUp, tactic, stream);
+  moesq::GemmParams d{};
+  d.a_codes = a2c; d.a_scales = a2s; d.a_global = a2_global; d.offsets = offsets; d.tile_offsets = tile_offsets;
+  d.rows = P; d.w_packed = w2->packed; d.w_mask = w2->mask; d.w_scale = w2->scale; d.w_global = w2->global;
+  d.E = E; d.N = H; d.K = I; d.G = 1; d.out = drows; d.topk_weights = topk_weights; d.sorted = sorted;
+  moesq::launch_grouped_gemm(d, moesq::kEpiDown, tactic, stream);
+  moesq::launch_combine(drows, inv, T, k, H, out, stream);
+  return check_launch(stream, (flags & MOESQ_FLAG_SYNC_CHECK) != 0);
+}
+
+moesq_status moesq_compress_weights(const float* w, int64_t N, int32_t K, uint8_t* packed, uint8_t* mask, uint8_t* scale,
+                                    float* global, hipStream_t stream) {
+  MOESQ_REQUIRE(N >= 1 && K >= 32 && K % 32 == 0, MOESQ_ERR_INVALID, "compress_weights: N >= 1, K % 32 == 0");
+  MOESQ_REQUIRE(w && packed && mask && scale && global, MOESQ_ERR_INVALID, "compress_weights: null pointer");
+  MOESQ_REQUIRE(aligned16(w) && ((uintptr_t)packed & 3) == 0 && ((uintptr_t)mask & 1) == 0 && ((uintptr_t)global & 3) == 0,
+                MOESQ_ERR_INVALID, "compress_weights: w 16-byte, packed 4-byte, mask 2-byte aligned");
+  moesq::launch_compress(w, N, K, packed, mask, scale, global, stream);
+  return check_launch(stream, false);
+}
+
+moesq_status moesq_validate_weights(const uint8_t* mask, int64_t rows, int32_t K, int32_t* bad, hipStream_t stream) {
+  MOESQ_REQUIRE(rows >= 0 && K > 0 && K % 32 == 0, MOESQ_ERR_INVALID, "validate_weights: K % 32 == 0");
+  MOESQ_REQUIRE(bad && (rows == 0 || mask), MOESQ_ERR_INVALID, "validate_weights: null pointer");
+  moesq::launch_validate(mask, rows * (K / 16), bad, stream);
+  return check_launch(stream, false);
+}
+
+moesq_status moesq_unpack_pair_bitmask(const uint8_t* packed, const uint8_t* mask, int64_t rows, int32_t K, uint8_t* dense,
+                                       int32_t* bad, hipStream_t stream) {
+  MOESQ_REQUIRE(rows >= 0 && K > 0 && K % 32 == 0, MOESQ_ERR_INVALID, "unpack: K % 32 == 0");
+  MOESQ_REQUIRE(bad && (rows == 0 || (packed && mask && dense)), MOESQ_ERR_INVALID, "unpack: null pointer");
+  MOESQ_REQUIRE(((uintptr_t)packed & 3) == 0 && ((uintptr_t)dense & 3) == 0, MOESQ_ERR_INVALID, "unpack: 4-byte alignment");
+  moesq::launch_unpack(packed, mask, rows * (K / 16), dense, bad, stream);
+  return check_launch(stream, false);
+}
+
+moesq_status moesq_pack_pair_bitmask(const uint8_t* dense, int64_t rows, int32_t K, uint8_t* packed, uint8_t* mask,
+                                     int32_t* bad, hipStream_t stream) {
+  MOESQ_REQUIRE(rows >= 0 && K > 0 && K % 32 == 0, MOESQ_ERR_INVALID, "pack: K % 32 == 0");
+  MOESQ_REQUIRE(bad && (rows == 0 || (packed && mask && dense)), MOESQ_ERR_INVALID, "pack: null pointer");
+  MOESQ_REQUIRE(((uintptr_t)packed & 3) == 0 && ((uintptr_t)dense & 3) == 0, MOESQ_ERR_INVALID, "pack: 4-byte alignment");
+  moesq::launch_pack(dense, rows * (K / 16), packed, mask, bad, stream);
+  return check_launch(stream, false);
+}
+
+}  // extern "C"

@@ -1,0 +1,162 @@
+// Device helpers of the MI355X (gfx950, wave64) paired-4:8 NVFP4 MoE kernels.
+//
+// Number formats (model card "Qwen3.5-397B-A17B-P48NVFP4-MoESQ", "Compression details"): NVFP4 is an
+// E2M1 value per element, an FP8-E4M3 scale per 32 dense K and an FP32 global scale; the value of a
+// code is e2m1(code) * e4m3(scale) * global.
+//
+// Exact decisions. Every rounding decision (the E4M3 scale of a 32-group and the E2M1 code of an
+// element) is taken on the exact real quotient, with ties to even, by sign tests of single fused
+// multiply-adds: sign(fma(-(b*s), g, |x|)) is the exact sign of |x| - b*s*g because b*s has at most
+// 7 significant bits (exact in fp32) and the FMA rounds once. This holds for finite inputs and
+// globals g >= 2^-90 (no underflow of the difference).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moesq {
+
+typedef _Float16 f16;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(16))) _Float16 f16x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+// ---------------------------------------------------------------------------------------------
+// E4M3FN (OCP FP8, bias 7, no infinities, 0x7F/0xFF NaN)
+// ---------------------------------------------------------------------------------------------
+
+// Non-negative finite E4M3 byte (0x00..0x7E) -> fp32, exact.
+__device__ __forceinline__ float e4m3_value(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  const float normal = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  const float sub = (float)m * 0x1p-9f;
+  return e ? normal : sub;
+}
+
+// Nearest E4M3 byte of fp32 v >= 0 (may be off by one step near a midpoint; callers fix it exactly).
+__device__ __forceinline__ int e4m3_candidate(float v) {
+  if (!(v < 448.0f)) return 0x7E;
+  if (v < 0x1p-6f) return (int)__builtin_rintf(v * 512.0f);            // subnormal steps of 2^-9
+  const uint32_t u = __float_as_uint(v);
+  const int e = (int)((u >> 23) & 255u) - 127;                         // v = 1.f * 2^e, e in [-6, 8]
+  const float mant = __uint_as_float((u & 0x007FFFFFu) | 0x3F800000u); // [1, 2)
+  const int m = (int)__builtin_rintf((mant - 1.0f) * 8.0f);           // 0..8 (8 carries)
+  const int c = ((e + 7) << 3) + m;
+  return c < 0x7E ? c : 0x7E;
+}
+
+// E4M3 byte of the exact quotient amax / (6 g): round to nearest, ties to even, saturating at 448.
+// amax >= 0, g > 0. The fp32 candidate is within one step; the two neighbouring midpoints m are
+// tested exactly with sign(fma(-(6m), g, amax)) (6m has <= 7 significant bits).
+__device__ __forceinline__ int scale_code(float amax, float g) {
+  int c = e4m3_candidate(amax / (6.0f * g));
+  if (c < 0x7E) {
+    const float mhi = 0.5f * (e4m3_value(c) + e4m3_value(c + 1));
+    const float dhi = __builtin_fmaf(-6.0f * mhi, g, amax);
+    if (dhi > 0.0f || (dhi == 0.0f && (c & 1))) return c + 1;
+  }
+  if (c > 0) {
+    const float mlo = 0.5f * (e4m3_value(c - 1) + e4m3_value(c));
+    const float dlo = __builtin_fmaf(-6.0f * mlo, g, amax);
+    if (dlo < 0.0f || (dlo == 0.0f && (c & 1))) return c - 1;
+  }
+  return c;
+}
+
+// E2M1 magnitude code (0..7) of the exact quotient ax / (s g): nearest, ties to even, saturating at 6.
+// Boundaries 0.25 .75 1.25 1.75 2.5 3.5 5; a tie goes to the even code (strict '>' where the lower
+// neighbour is even, '>=' where the upper one is). s == 0 gives 0.
+__device__ __forceinline__ uint32_t e2m1_code(float ax, float s, float g) {
+  if (s == 0.0f) return 0u;
+  uint32_t m = 0;
+  m += __builtin_fmaf(-0.25f * s, g, ax) > 0.0f;
+  m += __builtin_fmaf(-0.75f * s, g, ax) >= 0.0f;
+  m += __builtin_fmaf(-1.25f * s, g, ax) > 0.0f;
+  m += __builtin_fmaf(-1.75f * s, g, ax) >= 0.0f;
+  m += __builtin_fmaf(-2.5f * s, g, ax) > 0.0f;
+  m += __builtin_fmaf(-3.5f * s, g, ax) >= 0.0f;
+  m += __builtin_fmaf(-5.0f * s, g, ax) > 0.0f;
+  return m;
+}
+
+// 4-bit NVFP4 code of x for the group's scale value s and global g (sign bit copied from x).
+__device__ __forceinline__ uint32_t nvfp4_code(float x, float s, float g) {
+  return e2m1_code(__builtin_fabsf(x), s, g) | ((__float_as_uint(x) >> 28) & 8u);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// ---------------------------------------------------------------------------------------------
+// Operand decode for v_smfmac_f32_16x16x64_f16.
+//
+// K' order. Paired-4:8 keeps two of the four pairs of every 8-K chunk, so taking the even elements
+// of a chunk as one 4-group and the odd elements as the next gives exactly 2 kept elements per
+// 4-group, at the same positions (the kept pair ids i0 < i1) in both groups: the structured 2:4
+// pattern of the sparse MFMA. Activations are laid out in the same K' order
+// (e0 e2 e4 e6 | e1 e3 e5 e7 per chunk), which leaves every dot product unchanged.
+// ---------------------------------------------------------------------------------------------
+
+// Two fp4 codes of byte `sel` of w -> f16x2 (low nibble first), exact.
+template <int SEL>
+__device__ __forceinline__ f16x2 fp4x2_to_f16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
+}
+
+__device__ __forceinline__ uint32_t as_u32(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ f16x2 as_f16x2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
+
+// lo16(a) | lo16(b) << 16  and  hi16(a) | hi16(b) << 16
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
+
+// Dequantize the 8 codes of one activation chunk (one u32, low nibble = lower K) times scale s (f16)
+// into K' order: returns (e0 e2 | e4 e6 | e1 e3 | e5 e7) as 4 u32 of f16 pairs.
+__device__ __forceinline__ u32x4 act_chunk_kprime(uint32_t codes, f16x2 s2) {
+  const uint32_t d0 = as_u32(fp4x2_to_f16<0>(codes) * s2);
+  const uint32_t d1 = as_u32(fp4x2_to_f16<1>(codes) * s2);
+  const uint32_t d2 = as_u32(fp4x2_to_f16<2>(codes) * s2);
+  const uint32_t d3 = as_u32(fp4x2_to_f16<3>(codes) * s2);
+  u32x4 r;
+  r.x = pack_lo(d0, d1);
+  r.y = pack_lo(d2, d3);
+  r.z = pack_hi(d0, d1);
+  r.w = pack_hi(d2, d3);
+  return r;
+}
+
+// Compressed A operand of one smfmac from one u32 of kept bytes: bytes (b0 b1) of chunk 0 and
+// (b0' b1') of chunk 1. Slots 0,1 = (lo b0, lo b1) (evens of chunk 0), 2,3 = (hi b0, hi b1) (odds),
+// 4..7 the same for chunk 1, each times the block scale s (f16).
+__device__ __forceinline__ f16x8 weight_operand(uint32_t kept, f16x2 s2) {
+  const uint32_t c0 = as_u32(fp4x2_to_f16<0>(kept) * s2);
+  const uint32_t c1 = as_u32(fp4x2_to_f16<1>(kept) * s2);
+  const uint32_t c2 = as_u32(fp4x2_to_f16<2>(kept) * s2);
+  const uint32_t c3 = as_u32(fp4x2_to_f16<3>(kept) * s2);
+  u32x4 r;
+  r.x = pack_lo(c0, c1);
+  r.y = pack_hi(c0, c1);
+  r.z = pack_lo(c2, c3);
+  r.w = pack_hi(c2, c3);
+  return __builtin_bit_cast(f16x8, r);
+}
+
+// Sparse-index word of one smfmac from the mask byte of its two chunks: each chunk's nibble q (two
+// bits set, i0 < i1) gives the 4-bit code i0 | i1 << 2 for its even group and again for its odd group.
+__host__ __device__ inline uint32_t smfmac_index_of_mask_byte(uint32_t b) {
+  uint32_t out = 0;
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t q = (b >> (4 * h)) & 15u;
+    uint32_t i0 = 0, i1 = 0, seen = 0;
+    for (uint32_t i = 0; i < 4; ++i)
+      if (q & (1u << i)) { if (seen == 0) i0 = i; else i1 = i; ++seen; }
+    const uint32_t code = i0 | (i1 << 2);
+    out |= (code | (code << 4)) << (8 * h);
+  }
+  return out;
+}
+
+// f16 value of a non-negative E4M3 scale byte (exact: E4M3 lies inside f16's range and precision).
+__device__ __forceinline__ f16 e4m3_to_f16(uint32_t b) { return (f16)e4m3_value(b); }
+
+}  // namespace moesq

@@ -1,0 +1,65 @@
+// Host-side launchers shared between the kernel files and the C ABI layer.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moesq {
+
+enum { kQuantSingle = 0, kQuantOffsets = 1, kQuantPairs = 2 };
+
+void launch_quantize(const void* x, bool f32, int64_t rows, int K, int64_t stride, const int* src_row,
+                     const int* offsets, int E, const int* pair_of_row, const int* pair_expert,
+                     const int* row_limit, int k, const float* global, uint8_t* codes, uint8_t* scales,
+                     int mode, hipStream_t stream);
+void launch_compress(const float* w, int64_t N, int K, uint8_t* packed, uint8_t* mask, uint8_t* scale,
+                     float* global, hipStream_t stream);
+void launch_validate(const uint8_t* mask, int64_t nbytes, int* bad, hipStream_t stream);
+void launch_unpack(const uint8_t* packed, const uint8_t* mask, int64_t nbytes, uint8_t* dense, int* bad,
+                   hipStream_t stream);
+void launch_pack(const uint8_t* dense, int64_t nbytes, uint8_t* packed, uint8_t* mask, int* bad,
+                 hipStream_t stream);
+void launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t stream);
+
+// Permutation: counts[E], offsets[E+1], sorted[T*k] (live prefix), inv[T*k], tile_offsets[E+1]
+// (prefix of ceil(count/bm) for the grouped GEMM's m-blocks, when bm > 0) and status[0] (number of
+// ids outside [-1, E), which are dropped).
+void launch_permute(const int* ids, int64_t T, int k, int E, int* counts, int* offsets, int* sorted,
+                    int* inv, int* tile_offsets, int bm, int* status, hipStream_t stream);
+// tile_offsets from offsets for m-blocks of bm rows.
+void launch_tile_offsets(const int* offsets, int E, int bm, int* tile_offsets, hipStream_t stream);
+
+// Grouped sparse GEMM variants.
+enum { kEpiStore = 0, kEpiGateUp = 1, kEpiDown = 2 };
+enum { kTacticDecode = 0, kTacticPrefill = 1 };
+int tactic_rows_per_mblock(int tactic);
+
+struct GemmParams {
+  // B operand: activation codes [rows][K/2], scales [rows][K/32]; expert e owns rows offsets[e]..
+  const uint8_t* a_codes;
+  const uint8_t* a_scales;
+  const float* a_global;     // [E]
+  const int* offsets;        // [E+1]
+  const int* tile_offsets;   // [E+1], m-blocks of tactic_rows_per_mblock rows
+  int64_t rows;              // rows of A (upper bound of offsets[E])
+  // weights, pair-bitmask storage [E][N][K/4], [E][N][K/16], [E][N][K/32], global [E][G]
+  const uint8_t* w_packed;
+  const uint8_t* w_mask;
+  const uint8_t* w_scale;
+  const float* w_global;
+  int E, N, K, G;
+  // kEpiStore / kEpiDown: fp32 rows [rows][N]
+  float* out;
+  // kEpiGateUp: h = silu(gate) * up quantized with h_global[e] into h_codes [rows][N/4], h_scales [rows][N/64]
+  uint8_t* h_codes;
+  uint8_t* h_scales;
+  const float* h_global;
+  // kEpiDown: router weight of each sorted row = topk_weights[sorted[row]]
+  const float* topk_weights;
+  const int* sorted;
+};
+void launch_grouped_gemm(const GemmParams& p, int epi, int tactic, hipStream_t stream);
+
+// out[t][:] = sum_j D[inv[t*k + j]][:] (rows with inv < 0 skipped), in j order.
+void launch_combine(const float* D, const int* inv, int64_t T, int k, int H, float* out, hipStream_t stream);
+
+}  // namespace moesq

@@ -1,0 +1,86 @@
+"""Comparison of the HIP MoE FFN with the oracle, shared by the GPU tests, the smoke check and the bench.
+
+Bit-exact: the permutation and the gate/up input codes/scales (exact inputs, exact decisions).
+The down input (quantized h) may differ from the oracle only where the oracle's own decision lies
+within the HIP path's fp32 error bound of a rounding boundary (both neighbours are correct results);
+every such group must be one of the oracle's admissible encodings. The final output is compared
+row by row (max |y - yref| / max |yref| <= 1e-3) with the oracle's output computed from the admissible
+encoding the GPU picked, so a legitimate tie flip does not fail the test and anything else does.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import compress, moe, nvfp4
+
+TOL = 1e-3
+
+
+def oracle_layer(dense_expert, experts):
+    """Oracle's own compression of the dense weights of the given experts: (w13, w2) dicts-of-arrays."""
+    w13 = [dict(), dict(), dict(), dict()]
+    w2 = [dict(), dict(), dict(), dict()]
+    for e in experts:
+        g, u, d = (t.float().cpu().numpy() for t in dense_expert(e))
+        cg, cu, cd = compress.compress(g), compress.compress(u), compress.compress(d)
+        for i in range(3):
+            w13[i][e] = np.concatenate([cg[i], cu[i]])
+            w2[i][e] = cd[i]
+        w13[3][e] = np.array([cg[3], cu[3]], np.float32)
+        w2[3][e] = np.array([cd[3]], np.float32)
+    return w13, w2
+
+
+def gamma_for(K: int) -> float:
+    # fp32 accumulation of 64-K sparse-MFMA partial sums: K/64 additions plus the MFMA's own 32-term sum
+    return K / 64.0 + 64.0
+
+
+def compare_ffn(x, ids, wts, ow13, ow2, g13, g2, gpu_out, gpu, tokens=None, E=None):
+    """Check the GPU FFN against the oracle on ``tokens`` (all if None). ``gpu`` holds numpy copies of
+    the GPU intermediates (sorted, offsets, inv, a13_codes, a13_scales, a2_codes, a2_scales).
+    Returns a stats dict; raises AssertionError on any mismatch."""
+    x = np.asarray(x, np.float64)
+    T, H = x.shape
+    k = ids.shape[1]
+    E = len(g13) if E is None else E
+    tok = np.arange(T) if tokens is None else np.asarray(tokens)
+    xs, ids_s, wts_s = x[tok], ids[tok], wts[tok]
+    out_ref, inter = moe.moe_ffn(xs, ids_s, wts_s, ow13, ow2, g13, g2, want=True)
+    I = inter["h"].shape[1]
+    # subset sorted row -> GPU row
+    p_sub = inter["sorted_pairs"]
+    t_sub, j_sub = p_sub // k, p_sub % k
+    gpu_rows = gpu["inv"][tok[t_sub] * k + j_sub]
+    assert (gpu_rows >= 0).all()
+    assert np.array_equal(gpu["a13_codes"][gpu_rows], inter["a13_codes"]), "gate/up input codes differ"
+    assert np.array_equal(gpu["a13_scales"][gpu_rows], inter["a13_scales"]), "gate/up input scales differ"
+    a2c_gpu = gpu["a2_codes"][gpu_rows]
+    a2s_gpu = gpu["a2_scales"][gpu_rows]
+    same = (a2s_gpu == inter["a2_scales"]) & (
+        nvfp4.unpack_codes(a2c_gpu).reshape(-1, I // 32, 32) ==
+        nvfp4.unpack_codes(inter["a2_codes"]).reshape(-1, I // 32, 32)).all(axis=2)
+    n_diff = int((~same).sum())
+    adopted_c = inter["a2_codes"].copy()
+    adopted_s = inter["a2_scales"].copy()
+    if n_diff:
+        bound = moe.h_error_bound(xs, ids_s, ow13, g13, g2, gamma_for(H))
+        ge = np.asarray(g2, np.float64)[ids_s.ravel()[p_sub]]
+        ok = nvfp4.check_admissible(inter["h"], bound, ge, a2c_gpu, a2s_gpu)
+        bad = (~same) & (~ok)
+        assert not bad.any(), f"{int(bad.sum())} down-input groups are not an admissible encoding"
+        rows_d, grp_d = np.nonzero(~same)
+        cu = nvfp4.unpack_codes(adopted_c)
+        cg = nvfp4.unpack_codes(a2c_gpu)
+        for r, gi in zip(rows_d, grp_d):
+            cu[r, 32 * gi:32 * gi + 32] = cg[r, 32 * gi:32 * gi + 32]
+            adopted_s[r, gi] = a2s_gpu[r, gi]
+        adopted_c = (cu[:, 0::2] | (cu[:, 1::2] << 4)).astype(np.uint8)
+        out_ref = moe.down_combine(adopted_c, adopted_s, g2, inter["offsets"], p_sub, wts_s, ow2, len(tok), H)
+    y = np.asarray(gpu_out, np.float64)[tok]
+    err = np.abs(y - out_ref).max(axis=1) / np.maximum(np.abs(out_ref).max(axis=1), 1e-300)
+    nz = np.abs(out_ref).max(axis=1) > 0
+    worst = float(err[nz].max()) if nz.any() else 0.0
+    assert worst <= TOL, f"row-normwise error {worst:.3e} > {TOL}"
+    return {"rows": int(len(tok)), "max_row_rel_err": worst, "admissible_flips": n_diff,
+            "groups": int(same.size)}

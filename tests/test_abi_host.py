@@ -1,0 +1,100 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every declared symbol, and its
+synchronous argument checks return the documented status without launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+moesq = pytest.importorskip("sparse_quantized_moe_amd")
+if not os.path.exists(moesq.library_path):
+    pytest.skip("libmoesq.so not built (run python -m sparse_quantized_moe_amd.build)", allow_module_level=True)
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "moesq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moesq_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    L = moesq.lib()
+    decl = declared_symbols()
+    assert len(decl) >= 14
+    for name in decl:
+        assert hasattr(L, name), name
+    assert sorted(decl) == sorted(moesq.EXPORTED_SYMBOLS)
+    assert moesq.abi_version() == 1
+
+
+def test_status_strings():
+    L = moesq.lib()
+    for s, want in [(OK, b"ok"), (INVALID, b"invalid argument"), (UNSUPPORTED, b"unsupported shape"),
+                    (WORKSPACE, b"workspace too small"), (-4, b"HIP error")]:
+        assert L.moesq_status_string(s) == want
+
+
+def test_layout_is_aligned_and_ordered():
+    lay = moesq.ffn_layout(256, 2048, 768, 8, 128)
+    offs = [lay[n] for n in ("counts", "offsets", "tile_offsets", "status", "sorted", "inv", "a13_codes",
+                             "a13_scales", "a2_codes", "a2_scales", "down_rows")]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    P = 256 * 8
+    assert lay["down_rows"] + P * 2048 * 4 <= lay["total"]
+    assert lay["rows_per_mblock"] == 32                     # decode tactic for 16 rows per expert
+    assert moesq.ffn_layout(8192, 2048, 768, 8, 128)["rows_per_mblock"] == 128
+    assert moesq.lib().moesq_moe_ffn_workspace_size(256, 2048, 768, 8, 128, 0) == lay["total"]
+
+
+def _weights(E=2, N=64, K=256, G=1, ptr=16):
+    return moesq._CWeights(ptr, ptr, ptr, ptr, E, N, K, G)
+
+
+def test_argument_checks_return_status_without_launching():
+    L = moesq.lib()
+    P = ctypes.c_void_p(16)
+    # quantize: K not a multiple of 32, null pointers, bad dtype
+    assert L.moesq_quantize_act(P, 0, 4, 48, 48, None, None, 0, P, P, P, None) == INVALID
+    assert L.moesq_quantize_act(None, 0, 4, 64, 64, None, None, 0, P, P, P, None) == INVALID
+    assert L.moesq_quantize_act(P, 7, 4, 64, 64, None, None, 0, P, P, P, None) == INVALID
+    assert L.moesq_quantize_act(P, 0, 0, 64, 64, None, None, 0, P, P, P, None) == OK        # rows = 0: no-op
+    L.moesq_quantize_act(P, 0, 4, 48, 48, None, None, 0, P, P, P, None)
+    assert b"K must be a multiple of 32" in L.moesq_last_error()
+    # permute: k out of range, too many experts
+    assert L.moesq_permute(P, 4, 0, 8, P, P, P, P, P, None) == INVALID
+    assert L.moesq_permute(P, 4, 2, 2000, P, P, P, P, P, None) == UNSUPPORTED
+    # grouped GEMM: K % 256, G, workspace
+    w = _weights(K=96)
+    assert L.moesq_grouped_gemm(P, P, P, P, 4, ctypes.byref(w), P, P, 1 << 20, None) == UNSUPPORTED
+    w = _weights(G=3)
+    assert L.moesq_grouped_gemm(P, P, P, P, 4, ctypes.byref(w), P, P, 1 << 20, None) == INVALID
+    w = _weights()
+    assert L.moesq_grouped_gemm(P, P, P, P, 4, ctypes.byref(w), P, P, 4, None) == WORKSPACE
+    assert b"workspace" in L.moesq_last_error()
+    assert L.moesq_grouped_gemm(P, P, P, P, 4, None, P, P, 1 << 20, None) == INVALID
+    # moe_ffn: inconsistent shapes, missing fused gate|up, workspace
+    H, I, E = 256, 256, 4
+    w13 = _weights(E=E, N=2 * I, K=H, G=2)
+    w2 = _weights(E=E, N=H, K=I, G=1)
+    w2_bad = _weights(E=E, N=H + 64, K=I, G=1)
+    args = lambda a, b, ws: (P, 8, H, P, P, 2, ctypes.byref(a), ctypes.byref(b), P, P, P, P, ws, 0, None)
+    assert L.moesq_moe_ffn(*args(w13, w2_bad, 1 << 30)) == INVALID
+    assert L.moesq_moe_ffn(*args(_weights(E=E, N=2 * I, K=H, G=1), w2, 1 << 30)) == INVALID
+    assert L.moesq_moe_ffn(*args(w13, w2, 16)) == WORKSPACE
+    assert L.moesq_moe_ffn(P, 0, H, P, P, 2, ctypes.byref(w13), ctypes.byref(w2), P, P, P, P, 16, 0, None) == OK
+    # compress and codec
+    assert L.moesq_compress_weights(P, 4, 40, P, P, P, P, None) == INVALID
+    assert L.moesq_validate_weights(P, 4, 40, P, None) == INVALID
+    assert L.moesq_unpack_pair_bitmask(P, P, 4, 40, P, P, None) == INVALID
+    assert L.moesq_pack_pair_bitmask(P, 4, 40, P, P, P, None) == INVALID
+
+
+def test_binding_refuses_cpu_tensors():
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    with pytest.raises(moesq.MoesqError):
+        moesq.quantize_act(x, torch.ones(1))

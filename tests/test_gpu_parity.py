@@ -1,0 +1,302 @@
+"""Parity of the HIP library (through its C ABI) with the CPU oracle on MI355X.
+
+Integer work is compared bit-exactly (permutation, quantized codes and scales, compressed weights,
+storage codec); fp32 outputs row by row within 1e-3 (max |y - yref| / max |yref| per row).
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import compress, moe, nvfp4, pairbitmask
+
+pytestmark = pytest.mark.gpu
+
+moesq = pytest.importorskip("sparse_quantized_moe_amd")
+DEV = "cuda"
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    _need_gpu()
+    yield
+    torch.cuda.synchronize()
+
+
+def rowwise(y, ref):
+    y = np.asarray(y, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = np.maximum(np.abs(ref).max(axis=1), 1e-300)
+    return float((np.abs(y - ref).max(axis=1) / den).max())
+
+
+# ------------------------------------------------------------------------------------------------
+# activation quantizer
+# ------------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("T,H,outliers,gmode", [
+    (16, 512, 0.0, "amax"), (256, 2048, 0.0, "amax"), (64, 4096, 0.0, "fixed"),
+    (333, 7168, 0.001, "amax"), (5, 96, 0.0, "tiny"), (7, 64, 0.0, "huge")])
+def test_quantize_bf16_bit_exact(T, H, outliers, gmode):
+    x = synth.activations(3, T, H, device=DEV, outlier_frac=outliers, outlier_scale=50.0)
+    amax = np.float32(x.float().abs().max().item())
+    g = {"amax": amax / np.float32(2688), "fixed": synth.ACT_GLOBAL_FIXED,
+         "tiny": np.float32(2.0 ** -40), "huge": np.float32(100.0)}[gmode]
+    gt = torch.tensor([g], dtype=torch.float32, device=DEV)
+    codes, scales = moesq.quantize_act(x, gt)
+    rc, rs = nvfp4.quantize(x.float().cpu().numpy(), np.float64(g))
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
+def test_quantize_f32_boundaries_bit_exact():
+    """fp32 inputs placed on and next to every E2M1 and E4M3 rounding boundary."""
+    rng = np.random.default_rng(11)
+    R = 512
+    g = np.float32(0.0371)
+    x = np.zeros((R, 64), np.float32)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    for r in range(R):
+        s = float(nvfp4.E4M3_MAGNITUDES[rng.integers(8, 0x7E)])
+        for gi in range(2):
+            # make the group amax give exactly scale s (amax = 6 s g, a +-6 code)
+            v = (rng.choice(mids, 32) * s * float(g)).astype(np.float32)
+            v = np.where(rng.random(32) < 0.3, np.nextafter(v, np.float32(np.inf)), v)
+            v = np.where(rng.random(32) < 0.3, np.nextafter(v, np.float32(0)), v)
+            v[0] = np.float32(6 * s * float(g))
+            if rng.random() < 0.3:   # amax on an E4M3 midpoint instead
+                i = rng.integers(8, 0x7D)
+                m = (nvfp4.E4M3_MAGNITUDES[i] + nvfp4.E4M3_MAGNITUDES[i + 1]) / 2
+                v[0] = np.float32(6 * m * float(g))
+            v *= np.where(rng.random(32) < 0.5, -1, 1).astype(np.float32)
+            x[r, 32 * gi:32 * gi + 32] = v
+    xt = torch.from_numpy(x).to(DEV)
+    codes, scales = moesq.quantize_act(xt, torch.tensor([g], device=DEV))
+    rc, rs = nvfp4.quantize(x.astype(np.float64), np.float64(g))
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
+def test_quantize_gather_with_expert_globals():
+    T, H, E = 40, 256, 5
+    x = synth.activations(4, T, H, device=DEV)
+    src = torch.tensor(np.random.default_rng(0).integers(0, T, 70), dtype=torch.int32, device=DEV)
+    offs = torch.tensor([0, 10, 10, 33, 50, 66], dtype=torch.int32, device=DEV)
+    g = torch.tensor([0.001, 0.002, 0.0005, 0.004, 0.0011], dtype=torch.float32, device=DEV)
+    codes = torch.zeros((70, H // 2), dtype=torch.uint8, device=DEV)
+    codes, scales = moesq.quantize_act(x, g, src_row=src, expert_offsets=offs)
+    xs = x.float().cpu().numpy()[src.cpu().numpy()]
+    o = offs.cpu().numpy()
+    for e in range(E):
+        if o[e + 1] > o[e]:
+            rc, rs = nvfp4.quantize(xs[o[e]:o[e + 1]], np.float64(g[e].item()))
+            assert np.array_equal(codes[o[e]:o[e + 1]].cpu().numpy(), rc)
+            assert np.array_equal(scales[o[e]:o[e + 1]].cpu().numpy(), rs)
+
+
+# ------------------------------------------------------------------------------------------------
+# permutation
+# ------------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("T,k,E,kind", [(256, 8, 128, "softmax"), (8192, 8, 128, "zipf"), (1, 1, 1, "softmax"),
+                                        (1000, 10, 512, "softmax"), (16384, 8, 384, "zipf"), (3, 2, 1024, "softmax")])
+def test_permute_bit_exact(T, k, E, kind):
+    ids, _ = synth.routing(5, T, E, k, kind, 1.0, 1.0)
+    ids = ids.copy()
+    if T > 4:
+        ids[1, 0] = -1
+        ids[2, :] = -1
+    counts, offsets, sorted_, inv, status = moesq.permute(torch.from_numpy(ids).to(DEV), E)
+    rc, ro, rs, ri = moe.permute(ids, E)
+    n = int(ro[-1])
+    assert np.array_equal(counts.cpu().numpy(), rc)
+    assert np.array_equal(offsets.cpu().numpy(), ro)
+    assert np.array_equal(sorted_.cpu().numpy()[:n], rs)
+    assert np.array_equal(inv.cpu().numpy(), ri)
+    assert status.item() == 0
+
+
+def test_permute_duplicates_and_invalid_ids():
+    rng = np.random.default_rng(8)
+    T, k, E = 700, 4, 16
+    ids = rng.integers(-1, E, size=(T, k)).astype(np.int32)     # many duplicate ids inside rows
+    bad = ids.copy()
+    bad[5, 1] = E + 3
+    bad[600, 0] = -7
+    counts, offsets, sorted_, inv, status = moesq.permute(torch.from_numpy(bad).to(DEV), E)
+    ref_ids = bad.copy()
+    ref_ids[(ref_ids >= E) | (ref_ids < -1)] = -1
+    rc, ro, rs, ri = moe.permute(ref_ids, E)
+    assert np.array_equal(offsets.cpu().numpy(), ro)
+    assert np.array_equal(sorted_.cpu().numpy()[:int(ro[-1])], rs)
+    assert np.array_equal(inv.cpu().numpy(), ri)
+    assert status.item() == 2
+
+
+# ------------------------------------------------------------------------------------------------
+# weight compression and storage codec
+# ------------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("N,K", [(256, 512), (768, 2048), (64, 7168), (3, 32)])
+def test_compress_bit_exact(N, K):
+    w = synth.dense_weight(6, 0, 0, N, K, device=DEV)
+    if N == 3:                                   # ties between pair magnitudes and an all-zero chunk
+        w[0, :8] = torch.tensor([0.5, 0, 0, 0.5, -0.5, 0, 0.3, 0.4], device=DEV)
+        w[1, 8:16] = 0
+    packed, mask, scale, gw = moesq.compress_weights(w)
+    rp, rm, rs, rg = compress.compress(w.cpu().numpy())
+    assert gw.item() == rg
+    assert np.array_equal(scale.cpu().numpy(), rs)
+    assert np.array_equal(mask.cpu().numpy(), rm)
+    assert np.array_equal(packed.cpu().numpy(), rp)
+
+
+def test_storage_codec_bit_exact():
+    rng = np.random.default_rng(9)
+    N, K = 200, 1024
+    packed, mask, _, _ = synth.random_sparse_weights(10, 1, N, K)
+    p, m = torch.from_numpy(packed[0]).to(DEV), torch.from_numpy(mask[0]).to(DEV)
+    dense, bad = moesq.unpack_pair_bitmask(p, m, K)
+    assert bad.item() == 0
+    assert np.array_equal(dense.cpu().numpy(), pairbitmask.unpack(packed[0], mask[0]))
+    # pack of a dense tensor whose kept bytes are nonzero: round trip
+    d2 = pairbitmask.unpack(packed[0] | 1, mask[0])
+    p2, m2, bad2 = moesq.pack_pair_bitmask(torch.from_numpy(d2).to(DEV), K)
+    rp, rm = pairbitmask.pack(d2)
+    assert bad2.item() == 0 and np.array_equal(p2.cpu().numpy(), rp) and np.array_equal(m2.cpu().numpy(), rm)
+    # canonical completion of chunks with fewer than two nonzero bytes, and validation
+    d3 = d2.copy()
+    d3[0, :4] = 0
+    d3[1, 4:8] = [0, 0, 9, 0]
+    p3, m3, _ = moesq.pack_pair_bitmask(torch.from_numpy(d3).to(DEV), K)
+    rp3, rm3 = pairbitmask.pack(d3)
+    assert np.array_equal(p3.cpu().numpy(), rp3) and np.array_equal(m3.cpu().numpy(), rm3)
+    mbad = mask[0].copy()
+    mbad[3, 2] = 0x37
+    mbad[9, 0] = 0xFF
+    assert moesq.validate_weights(torch.from_numpy(mbad).to(DEV), K) == pairbitmask.invalid_nibbles(mbad) == 3
+
+
+# ------------------------------------------------------------------------------------------------
+# grouped GEMM
+# ------------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("E,N,K,G,counts", [
+    (1, 256, 512, 1, [16]),                                       # one expert linear
+    (4, 256, 512, 2, [0, 5, 33, 17]),                             # ragged, an empty expert, decode tactic
+    (3, 320, 768, 1, [200, 0, 130]),                              # prefill tactic, N not a multiple of 256
+    (2, 64, 2048, 2, [1, 129]),
+])
+def test_grouped_gemm_random_bytes(E, N, K, G, counts):
+    packed, mask, scale, gw = synth.random_sparse_weights(12, E, N, K, G)
+    scale = np.clip(scale, 0x18, 0x60).astype(np.uint8)            # keep products in a sane exponent range
+    rows = sum(counts)
+    a_codes, a_scales = synth.random_act_codes(13, rows, K)
+    a_scales = np.clip(a_scales, 0x18, 0x60).astype(np.uint8)
+    a_global = (2.0 ** np.random.default_rng(1).uniform(-6, -2, E)).astype(np.float32)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    w = moesq.SparseWeights(*(torch.from_numpy(np.ascontiguousarray(t)).to(DEV) for t in (packed, mask, scale, gw)))
+    out = moesq.grouped_gemm(torch.from_numpy(a_codes).to(DEV), torch.from_numpy(a_scales).to(DEV),
+                             torch.from_numpy(a_global).to(DEV), torch.from_numpy(offsets).to(DEV), w)
+    ref = moe.grouped_gemm(a_codes, a_scales, a_global, offsets, packed, mask, scale, gw)
+    err = rowwise(out.cpu().numpy(), ref)
+    assert err <= 1e-3, err
+
+
+def test_linear_workload():
+    """One expert linear, M=16, N=256, K=512, compressed from N(0, 0.02) and quantized from N(0, 1)."""
+    wl = synth.WORKLOADS["linear"]
+    w = synth.dense_weight(0, 0, 0, wl.I, wl.H, device=DEV)
+    packed, mask, scale, gw = moesq.compress_weights(w)
+    rp, rm, rs, rg = compress.compress(w.cpu().numpy())
+    assert np.array_equal(packed.cpu().numpy(), rp) and np.array_equal(mask.cpu().numpy(), rm)
+    assert np.array_equal(scale.cpu().numpy(), rs) and gw.item() == rg
+    x = synth.activations(0, wl.T, wl.H, device=DEV)
+    g = np.float32(x.float().abs().max().item()) / np.float32(2688)
+    codes, scales = moesq.quantize_act(x, torch.tensor([g], device=DEV))
+    rc, rsc = nvfp4.quantize(x.float().cpu().numpy(), np.float64(g))
+    assert np.array_equal(codes.cpu().numpy(), rc) and np.array_equal(scales.cpu().numpy(), rsc)
+    sw = moesq.SparseWeights(packed[None], mask[None], scale[None], gw.view(1, 1))
+    offs = torch.tensor([0, wl.T], dtype=torch.int32, device=DEV)
+    out = moesq.grouped_gemm(codes, scales, torch.tensor([g], device=DEV), offs, sw)
+    ref = moe.grouped_gemm(rc, rsc, [g], [0, wl.T], rp[None], rm[None], rs[None], np.array([[rg]]))
+    assert rowwise(out.cpu().numpy(), ref) <= 1e-3
+
+
+# ------------------------------------------------------------------------------------------------
+# MoE FFN
+# ------------------------------------------------------------------------------------------------
+def _layer(seed, E, H, I):
+    def dense_expert(e):       # regenerated on demand (deterministic), not cached
+        return synth.expert_dense_weights(seed, e, H, I, device=DEV)
+    w13, w2 = moesq.compress_moe_layer(E, H, I, dense_expert, device=DEV)
+    return w13, w2, dense_expert
+
+
+def _globals(x, ids, E, dense_expert, fixed=False):
+    if fixed:
+        return (np.full(E, synth.ACT_GLOBAL_FIXED, np.float32),) * 2
+    g13 = synth.act_globals_from_x(x, ids, E)
+    g2 = np.full(E, synth.ACT_GLOBAL_FIXED, np.float32)
+    T = x.shape[0]
+    for e in range(E):
+        rows = np.nonzero((ids == e).any(axis=1))[0]
+        if len(rows):
+            g, u, _ = dense_expert(e)
+            g2[e] = synth.down_global_from_dense(x[torch.from_numpy(rows).to(x.device)], g, u)
+    return g13, g2
+
+
+def _run_ffn(x, ids, wts, w13, w2, g13, g2):
+    T, H = x.shape
+    k = ids.shape[1]
+    E, I = w13.E, w2.K
+    ws = torch.empty(moesq.lib().moesq_moe_ffn_workspace_size(T, H, I, k, E, 0), dtype=torch.uint8, device=DEV)
+    out = moesq.moe_ffn(x, torch.from_numpy(ids).to(DEV), torch.from_numpy(wts).to(DEV), w13, w2,
+                        torch.from_numpy(g13).to(DEV), torch.from_numpy(g2).to(DEV), workspace=ws)
+    inter = {kk: v.cpu().numpy() for kk, v in moesq.ffn_intermediates(ws, T, H, I, k, E).items()}
+    return out.cpu().numpy(), inter
+
+
+@pytest.mark.parametrize("E,H,I,T,k,fixed", [(8, 512, 256, 64, 4, False),     # decode tactic
+                                              (8, 512, 256, 512, 4, False),    # prefill tactic
+                                              (6, 256, 512, 40, 3, True)])     # saturating 1/2688 globals
+def test_moe_ffn_small(E, H, I, T, k, fixed):
+    from ffn_check import compare_ffn, oracle_layer
+    w13, w2, dense_expert = _layer(21, E, H, I)
+    x = synth.activations(22, T, H, device=DEV)
+    ids, wts = synth.routing(23, T, E, k)
+    g13, g2 = _globals(x, ids, E, dense_expert, fixed)
+    out, inter = _run_ffn(x, ids, wts, w13, w2, g13, g2)
+    rc, ro, rs, ri = moe.permute(ids, E)
+    assert np.array_equal(inter["offsets"], ro) and np.array_equal(inter["inv"], ri)
+    assert np.array_equal(inter["sorted"][:int(ro[-1])], rs)
+    ow13, ow2 = oracle_layer(dense_expert, range(E))
+    st = compare_ffn(x.float().cpu().numpy(), ids, wts, ow13, ow2, g13, g2, out, inter)
+    print("ffn small", E, H, I, T, k, st)
+
+
+@pytest.mark.parametrize("name,ntok", [("qwen3_30b_decode", 3), ("e512_decode", 1)])
+def test_moe_ffn_full_size_sampled(name, ntok):
+    """Full-size decode layers; integer intermediates checked on every row, outputs on sampled tokens."""
+    from ffn_check import compare_ffn, oracle_layer
+    wl = synth.WORKLOADS[name]
+    w13, w2, dense_expert = _layer(0, wl.E, wl.H, wl.I)
+    x = synth.activations(0, wl.T, wl.H, device=DEV)
+    ids, wts = synth.routing(0, wl.T, wl.E, wl.k, wl.routing, wl.zipf_s, wl.zipf_beta)
+    g13, g2 = _globals(x, ids, wl.E, dense_expert, wl.fixed_act_global)
+    out, inter = _run_ffn(x, ids, wts, w13, w2, g13, g2)
+    rc, ro, rs, ri = moe.permute(ids, wl.E)
+    assert np.array_equal(inter["offsets"], ro) and np.array_equal(inter["inv"], ri)
+    # every gate/up input row, bit-exact
+    P = int(ro[-1])
+    e_row = ids.ravel()[rs]
+    xr = x.float().cpu().numpy()[rs // wl.k]
+    rc13, rs13 = nvfp4.quantize(xr, g13[e_row].astype(np.float64))
+    assert np.array_equal(inter["a13_codes"][:P], rc13) and np.array_equal(inter["a13_scales"][:P], rs13)
+    toks = np.random.default_rng(1).choice(wl.T, ntok, replace=False)
+    touched = sorted(set(ids[toks].ravel().tolist()))
+    ow13, ow2 = oracle_layer(dense_expert, touched)
+    st = compare_ffn(x.float().cpu().numpy(), ids, wts, ow13, ow2, g13, g2, out, inter, tokens=toks)
+    print(name, st)
