@@ -1,0 +1,296 @@
+#!/usr/bin/env python3
+"""Throughput of the paired-4:8 sparse NVFP4 MoE FFN on one MI355X.
+
+Metric: weight-stream GB/s at decode (stored sparse bytes of the experts a batch touches, per second
+of the whole moesq_moe_ffn call) on the 128-expert, top-8, hidden-2048, moe_intermediate-768 layer at
+T=256 tokens, and effective dense TFLOP/s (6*P*H*I per second, P = T*k) of the same layer at
+prefill, T=8192 with Zipf(1.1)-skewed routing.
+
+One step = one moesq_moe_ffn call (permute, quantize, gate/up GEMM + SiLU*up + quantize, down GEMM,
+top-k combine) over one batch already resident in HBM. The layer's weights (207.6 MB) fit in the
+256 MB Infinity Cache, so decode steps rotate over several copies of the weights (a cold-cache
+stream, the reported value) and the warm single-copy figure is reported beside it.
+
+Output: one JSON line (rank 0). ``roofline`` is for the dominant kernel (the gate/up GEMM), timed with
+HIP events recorded by the library on its own stream; ``cpu_baseline`` times the CPU oracle on a
+bounded sample of the same decode workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+F16_DENSE_PEAK_TFLOPS = 2500.0  # MI355X dense f16/bf16 MFMA (the sparse MFMA doubles the dense-equivalent rate)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            if self.hip.hipEventCreate(ctypes.byref(arr, i * ctypes.sizeof(ctypes.c_void_p))) != 0:
+                raise RuntimeError("hipEventCreate failed")
+        return arr
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, arr):
+        for h in arr:
+            self.hip.hipEventDestroy(h)
+
+
+def build_layer(wl, seed, dev):
+    import torch
+    import sparse_quantized_moe_amd as moesq
+    import synth
+
+    def dense_expert(e):
+        return synth.expert_dense_weights(seed, e, wl.H, wl.I, device=dev)
+    t0 = time.time()
+    w13, w2 = moesq.compress_moe_layer(wl.E, wl.H, wl.I, dense_expert, device=dev)
+    torch.cuda.synchronize()
+    log(f"layer {wl.name}: compressed {wl.E} experts in {time.time() - t0:.1f}s "
+        f"({(w13.nbytes() + w2.nbytes()) / 1e6:.1f} MB sparse storage)")
+    return w13, w2, dense_expert
+
+
+def batch(wl, seed, dev, dense_expert):
+    import torch
+    import synth
+    x = synth.activations(seed, wl.T, wl.H, device=dev, outlier_frac=wl.outlier_frac, outlier_scale=wl.outlier_scale)
+    ids, wts = synth.routing(seed, wl.T, wl.E, wl.k, wl.routing, wl.zipf_s, wl.zipf_beta)
+    if wl.fixed_act_global:
+        g13 = np.full(wl.E, synth.ACT_GLOBAL_FIXED, np.float32)
+        g2 = g13.copy()
+    else:
+        g13 = synth.act_globals_from_x(x, ids, wl.E)
+        g2 = np.full(wl.E, synth.ACT_GLOBAL_FIXED, np.float32)
+        for e in np.unique(ids):
+            rows = np.nonzero((ids == e).any(axis=1))[0]
+            g, u, _ = dense_expert(int(e))
+            g2[e] = synth.down_global_from_dense(x[torch.from_numpy(rows).to(dev)], g, u)
+    return x, ids, wts, g13, g2
+
+
+def touched_bytes(ids, E, H, I):
+    """Stored sparse bytes of the experts with >= 1 row: 3*H*I*11/32 per expert + fp32 globals (3)."""
+    n = len(np.unique(ids[ids >= 0]))
+    per = (2 * I * H + H * I) * 11 // 32 + 4 * 3
+    return n, n * per
+
+
+def run_steps(moesq, torch, ev, x, ids_t, wts_t, layers, g13_t, g2_t, out, ws, warmup, steps):
+    """Untimed warmup, then exactly ``steps`` timed calls bracketed by synchronizations.
+    Returns (wall seconds, per-step stage times [steps][5] in ms)."""
+    nl = len(layers)
+    for i in range(warmup):
+        w13, w2 = layers[i % nl]
+        moesq.moe_ffn(x, ids_t, wts_t, w13, w2, g13_t, g2_t, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    evs = [ev.create(6) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        w13, w2 = layers[i % nl]
+        moesq.set_stage_events(evs[i])
+        moesq.moe_ffn(x, ids_t, wts_t, w13, w2, g13_t, g2_t, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    moesq.set_stage_events(None)
+    stages = np.array([[ev.elapsed_ms(e[j], e[j + 1]) for j in range(5)] for e in evs])
+    total = np.array([ev.elapsed_ms(e[0], e[5]) for e in evs])
+    for e in evs:
+        ev.destroy(e)
+    return wall, stages, total
+
+
+def cpu_baseline(wl, seed, x, ids, wts, g13, g2, dense_expert, ntok):
+    """The oracle (unchanged) on a bounded sample of the decode batch: ntok tokens and their experts."""
+    import multiprocessing
+    from concurrent.futures import ProcessPoolExecutor
+    from oracle import compress, moe
+    import threadpoolctl
+
+    rng = np.random.default_rng(seed)
+    toks = np.sort(rng.choice(wl.T, ntok, replace=False))
+    experts = sorted(set(ids[toks].ravel().tolist()) - {-1})
+    dense = {e: [t.cpu().numpy() for t in dense_expert(e)] for e in experts}
+    t0 = time.time()
+    jobs = [(e, i) for e in experts for i in range(3)]
+    with ProcessPoolExecutor(max_workers=min(16, os.cpu_count() or 1),
+                             mp_context=multiprocessing.get_context("spawn")) as ex:
+        res = list(ex.map(compress.compress, [dense[e][i] for e, i in jobs]))
+    log(f"cpu baseline: oracle compression of {len(experts)} experts (not timed) {time.time() - t0:.1f}s")
+    by = {(e, i): r for (e, i), r in zip(jobs, res)}
+    w13 = [dict(), dict(), dict(), dict()]
+    w2 = [dict(), dict(), dict(), dict()]
+    for e in experts:
+        cg, cu, cd = by[(e, 0)], by[(e, 1)], by[(e, 2)]
+        for i in range(3):
+            w13[i][e] = np.concatenate([cg[i], cu[i]])
+            w2[i][e] = cd[i]
+        w13[3][e] = np.array([cg[3], cu[3]], np.float32)
+        w2[3][e] = np.array([cd[3]], np.float32)
+    xs = x.float().cpu().numpy()[toks]
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    t0 = time.perf_counter()
+    moe.moe_ffn(xs, ids[toks], wts[toks], w13, w2, g13, g2)
+    dt = time.perf_counter() - t0
+    n, nbytes = touched_bytes(ids[toks], wl.E, wl.H, wl.I)
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{ntok} of {wl.T} tokens of {wl.name} ({n} experts, {nbytes / 1e6:.1f} MB stored), "
+                      f"{dt:.2f}s fp64 NumPy"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3_30b_decode")
+    ap.add_argument("--prefill-workload", default="qwen3_30b_prefill", help="'' to skip the prefill figure")
+    ap.add_argument("--copies", type=int, default=4, help="weight copies rotated at decode (cache-cold stream)")
+    ap.add_argument("--cpu-tokens", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs the expert path on one GPU only; --gpus {args.gpus} is not supported "
+              "(the multi-GPU sharding is described, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparse_quantized_moe_amd as moesq
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ev = HipEvents()
+    wl = synth.WORKLOADS[args.workload]
+    w13, w2, dense_expert = build_layer(wl, args.seed, dev)
+    layers = [(w13, w2)]
+    for _ in range(args.copies - 1):
+        layers.append((moesq.SparseWeights(*(t.clone() for t in (w13.packed, w13.mask, w13.scale, w13.global_scale))),
+                       moesq.SparseWeights(*(t.clone() for t in (w2.packed, w2.mask, w2.scale, w2.global_scale)))))
+    x, ids, wts, g13, g2 = batch(wl, args.seed, dev, dense_expert)
+    ids_t, wts_t = torch.from_numpy(ids).to(dev), torch.from_numpy(wts).to(dev)
+    g13_t, g2_t = torch.from_numpy(g13).to(dev), torch.from_numpy(g2).to(dev)
+    ws = torch.empty(moesq.lib().moesq_moe_ffn_workspace_size(wl.T, wl.H, wl.I, wl.k, wl.E, 0), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty((wl.T, wl.H), dtype=torch.float32, device=dev)
+
+    wall, stages, total = run_steps(moesq, torch, ev, x, ids_t, wts_t, layers, g13_t, g2_t, out, ws,
+                                    args.warmup, args.steps)
+    ms = wall / args.steps * 1e3
+    n_touched, wbytes = touched_bytes(ids, wl.E, wl.H, wl.I)
+    value = wbytes / (wall / args.steps) / 1e9
+    st_mean = stages.mean(axis=0)
+    log("decode stage ms (mean): " + ", ".join(f"{n}={v * 1e3:.1f}us" for n, v in zip(moesq.FFN_STAGES, st_mean)))
+    log(f"decode: {ms * 1e3:.1f} us/step wall, {total.mean() * 1e3:.1f} us/step events, {value:.1f} GB/s")
+    # warm (single copy) figure
+    wall_w, _, total_w = run_steps(moesq, torch, ev, x, ids_t, wts_t, layers[:1], g13_t, g2_t, out, ws,
+                                   args.warmup, args.steps)
+    warm = wbytes / (wall_w / args.steps) / 1e9
+    # dominant kernel: gate/up GEMM; algorithmic bytes = W13 stored bytes of touched experts + its
+    # activation input (codes + scales) + its output (down-input codes + scales)
+    P = int((ids >= 0).sum())
+    w13_bytes = n_touched * (2 * wl.I * wl.H * 11 // 32 + 8)
+    gemm_bytes = w13_bytes + P * (wl.H // 2 + wl.H // 32) + P * (wl.I // 2 + wl.I // 32)
+    gemm_ms = float(st_mean[2])
+    achieved = gemm_bytes / (gemm_ms * 1e-3) / 1e9
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", "traffic_gemm_gate_up_qwen3_30b_decode.json")
+    if os.path.exists(tfile):
+        t = json.load(open(tfile))
+        if t.get("kernel_source_sha") == _kernel_sha():
+            traffic = t.get("bytes_per_launch")
+    result = {
+        "metric": "MoE FFN effective dense TFLOP/s (prefill) + weight-stream GB/s (decode), 1 GPU",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "nvfp4 w4a4 (f16 sparse MFMA, fp32 accumulate)", "data": "synthetic (seeded; random-init weights)",
+        "config": {"workload": wl.name, "experts": wl.E, "top_k": wl.k, "hidden": wl.H, "moe_intermediate": wl.I,
+                   "tokens": wl.T, "experts_touched": n_touched, "stored_bytes_streamed": wbytes,
+                   "weight_copies_rotated": args.copies, "warm_cache_GBps": round(warm, 2),
+                   "stage_us": {n: round(float(v) * 1e3, 2) for n, v in zip(moesq.FFN_STAGES, st_mean)}},
+        "roofline": {"bound": "hbm", "kernel": "k_grouped_gemm<gate_up> (decode tactic)", "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes_per_launch": gemm_bytes,
+                     "avg_launch_us": round(gemm_ms * 1e3, 2)},
+    }
+    del layers[1:]
+    torch.cuda.empty_cache()
+
+    if args.prefill_workload:
+        pw = synth.WORKLOADS[args.prefill_workload]
+        if (pw.E, pw.H, pw.I) != (wl.E, wl.H, wl.I):
+            w13, w2, dense_expert = build_layer(pw, args.seed, dev)
+        px, pids, pwts, pg13, pg2 = batch(pw, args.seed, dev, dense_expert)
+        pws = torch.empty(moesq.lib().moesq_moe_ffn_workspace_size(pw.T, pw.H, pw.I, pw.k, pw.E, 0),
+                          dtype=torch.uint8, device=dev)
+        pout = torch.empty((pw.T, pw.H), dtype=torch.float32, device=dev)
+        psteps = max(3, min(args.steps, 20))
+        pwall, pst, ptot = run_steps(moesq, torch, ev, px, torch.from_numpy(pids).to(dev),
+                                     torch.from_numpy(pwts).to(dev), [(w13, w2)], torch.from_numpy(pg13).to(dev),
+                                     torch.from_numpy(pg2).to(dev), pout, pws, min(args.warmup, 3), psteps)
+        PP = int((pids >= 0).sum())
+        eff = 6.0 * PP * pw.H * pw.I / (pwall / psteps) / 1e12
+        pst_mean = pst.mean(axis=0)
+        g_ms = float(pst_mean[2])
+        alg_flops = 2.0 * PP * (2 * pw.I) * pw.H / 2          # multiply-adds on the kept half of W13
+        ach = alg_flops / (g_ms * 1e-3) / 1e12
+        log("prefill stage ms (mean): " + ", ".join(f"{n}={v:.3f}ms" for n, v in zip(moesq.FFN_STAGES, pst_mean)))
+        log(f"prefill: {pwall / psteps * 1e3:.3f} ms/step, {eff:.1f} effective dense TFLOP/s")
+        result["prefill"] = {
+            "workload": pw.name, "tokens": pw.T, "value": round(eff, 2), "unit": "effective dense TFLOP/s",
+            "ms_per_step": round(pwall / psteps * 1e3, 4), "steps": psteps,
+            "stage_ms": {n: round(float(v), 4) for n, v in zip(moesq.FFN_STAGES, pst_mean)},
+            "roofline": {"bound": "mfma", "kernel": "k_grouped_gemm<gate_up> (prefill tactic)",
+                         "achieved": round(ach, 2), "peak": F16_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(ach / F16_DENSE_PEAK_TFLOPS, 4), "traffic": None,
+                         "algorithmic_flops_per_launch": alg_flops, "avg_launch_ms": round(g_ms, 4)},
+        }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, args.seed, x, ids, wts, g13, g2, dense_expert, args.cpu_tokens)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+def _kernel_sha() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "moesq_device.h"):
+        h.update(open(os.path.join(ROOT, "sparse_quantized_moe_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()

@@ -135,6 +135,13 @@ moesq_status moesq_moe_ffn(const void *x, int64_t T, int32_t H, const int32_t *t
                            float *out, void *workspace, size_t workspace_bytes, uint32_t flags,
                            hipStream_t stream);
 
+/* Profiling aid: with events (host array of n >= 6 hipEvent_t created by the caller) set, every later
+ * moesq_moe_ffn call on this host thread records events[0] on its stream before its first kernel and
+ * events[1..5] after the permutation, the gate/up input quantization, the gate/up GEMM (with the
+ * fused SiLU*up and down-input quantization), the down GEMM and the top-k combine. NULL disables it.
+ * The library keeps the pointer (thread-local) until it is reset; the caller keeps the array alive. */
+moesq_status moesq_set_stage_events(hipEvent_t *events /* host */, int32_t n);
+
 /* Weight compression of a dense fp32 linear [N][K] into pair-bitmask NVFP4 (the synthetic-layer
  * recipe; model card "Compression details": paired 4:8 along K, 2 of every 4 pairs kept): in each
  * 8-K chunk keep the 2 pairs with the largest a*a + b*b (float64, ties to the lower pair),

@@ -32,7 +32,7 @@ EXPORTED_SYMBOLS = (
     "moesq_abi_version", "moesq_status_string", "moesq_last_error", "moesq_quantize_act", "moesq_permute",
     "moesq_grouped_gemm_workspace_size", "moesq_grouped_gemm", "moesq_moe_ffn_layout",
     "moesq_moe_ffn_workspace_size", "moesq_moe_ffn", "moesq_compress_weights", "moesq_validate_weights",
-    "moesq_unpack_pair_bitmask", "moesq_pack_pair_bitmask",
+    "moesq_unpack_pair_bitmask", "moesq_pack_pair_bitmask", "moesq_set_stage_events",
 )
 
 
@@ -73,6 +73,7 @@ def _declare(L: ctypes.CDLL) -> None:
         "moesq_validate_weights": (ctypes.c_int, [_P, _I64, _I32, _P, _P]),
         "moesq_unpack_pair_bitmask": (ctypes.c_int, [_P, _P, _I64, _I32, _P, _P, _P]),
         "moesq_pack_pair_bitmask": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _P, _P]),
+        "moesq_set_stage_events": (ctypes.c_int, [_P, _I32]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -284,6 +285,22 @@ def compress_moe_layer(E: int, H: int, I: int, dense_expert, device="cuda"):
         compress_weights(u.contiguous(), w13.packed[e, I:], w13.mask[e, I:], w13.scale[e, I:], w13.global_scale[e, 1:2])
         compress_weights(d.contiguous(), w2.packed[e], w2.mask[e], w2.scale[e], w2.global_scale[e, 0:1])
     return w13, w2
+
+
+#: Stages of one moe_ffn call, in the order set_stage_events() brackets them.
+FFN_STAGES = ("permute", "quantize_x", "gemm_gate_up", "gemm_down", "combine")
+
+
+def set_stage_events(events) -> None:
+    """Record HIP events around the stages of later moe_ffn calls on this thread: ``events`` is a
+    ctypes array of >= 6 hipEvent_t handles (None disables)."""
+    if events is None:
+        _check(lib().moesq_set_stage_events(None, 0))
+    else:
+        _check(lib().moesq_set_stage_events(ctypes.cast(events, ctypes.c_void_p), len(events)))
+
+
+__all__ += ["FFN_STAGES", "set_stage_events"]
 
 
 def validate_weights(mask: torch.Tensor, K: int) -> int:

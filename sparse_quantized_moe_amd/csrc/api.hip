@@ -8,6 +8,11 @@
 namespace {
 
 thread_local std::string g_last_error;
+thread_local hipEvent_t* g_stage_events = nullptr;
+
+void stage_event(int i, hipStream_t stream) {
+  if (g_stage_events) (void)hipEventRecord(g_stage_events[i], stream);
+}
 
 moesq_status fail(moesq_status s, const char* fmt, const char* what) {
   char buf[512];
@@ -66,6 +71,12 @@ const char* moesq_status_string(moesq_status s) {
 }
 
 const char* moesq_last_error(void) { return g_last_error.c_str(); }
+
+moesq_status moesq_set_stage_events(hipEvent_t* events, int32_t n) {
+  MOESQ_REQUIRE(!events || n >= 6, MOESQ_ERR_INVALID, "set_stage_events: need at least 6 events");
+  g_stage_events = events;
+  return MOESQ_OK;
+}
 
 moesq_status moesq_quantize_act(const void* x, moesq_dtype x_dtype, int64_t rows, int32_t K, int64_t x_row_stride,
                                 const int32_t* src_row, const int32_t* expert_offsets, int32_t E, const float* global,
@@ -193,20 +204,26 @@ moesq_status moesq_moe_ffn(const void* x, int64_t T, int32_t H, const int32_t* t
   const int tactic = ffn_tactic(T, k, E);
   const int64_t P = T * k;
 
+  stage_event(0, stream);
   moesq::launch_permute(topk_ids, T, k, E, counts, offsets, sorted, inv, tile_offsets, L.rows_per_mblock, status, stream);
+  stage_event(1, stream);
   moesq::launch_quantize(x, false, P, H, H, nullptr, nullptr, E, sorted, topk_ids, offsets + E, k, a13_global, a13c,
                          a13s, moesq::kQuantPairs, stream);
+  stage_event(2, stream);
   moesq::GemmParams g{};
   g.a_codes = a13c; g.a_scales = a13s; g.a_global = a13_global; g.offsets = offsets; g.tile_offsets = tile_offsets;
   g.rows = P; g.w_packed = w13->packed; g.w_mask = w13->mask; g.w_scale = w13->scale; g.w_global = w13->global;
   g.E = E; g.N = w13->N; g.K = H; g.G = 2; g.h_codes = a2c; g.h_scales = a2s; g.h_global = a2_global;
   moesq::launch_grouped_gemm(g, moesq::kEpiGateUp, tactic, stream);
+  stage_event(3, stream);
   moesq::GemmParams d{};
   d.a_codes = a2c; d.a_scales = a2s; d.a_global = a2_global; d.offsets = offsets; d.tile_offsets = tile_offsets;
   d.rows = P; d.w_packed = w2->packed; d.w_mask = w2->mask; d.w_scale = w2->scale; d.w_global = w2->global;
   d.E = E; d.N = H; d.K = I; d.G = 1; d.out = drows; d.topk_weights = topk_weights; d.sorted = sorted;
   moesq::launch_grouped_gemm(d, moesq::kEpiDown, tactic, stream);
+  stage_event(4, stream);
   moesq::launch_combine(drows, inv, T, k, H, out, stream);
+  stage_event(5, stream);
   return check_launch(stream, (flags & MOESQ_FLAG_SYNC_CHECK) != 0);
 }
 
