@@ -73,6 +73,8 @@ def build_layer(wl, seed, dev):
         return synth.expert_dense_weights(seed, e, wl.H, wl.I, device=dev)
     t0 = time.time()
     w13, w2 = moesq.compress_moe_layer(wl.E, wl.H, wl.I, dense_expert, device=dev)
+    # load-time re-tiling into the kernels' layout (the same bytes)
+    w13, w2 = moesq.prepare_weights(w13), moesq.prepare_weights(w2)
     torch.cuda.synchronize()
     log(f"layer {wl.name}: compressed {wl.E} experts in {time.time() - t0:.1f}s "
         f"({(w13.nbytes() + w2.nbytes()) / 1e6:.1f} MB sparse storage)")
@@ -196,8 +198,8 @@ def main():
     w13, w2, dense_expert = build_layer(wl, args.seed, dev)
     layers = [(w13, w2)]
     for _ in range(args.copies - 1):
-        layers.append((moesq.SparseWeights(*(t.clone() for t in (w13.packed, w13.mask, w13.scale, w13.global_scale))),
-                       moesq.SparseWeights(*(t.clone() for t in (w2.packed, w2.mask, w2.scale, w2.global_scale)))))
+        layers.append(tuple(moesq.SparseWeights(w.packed.clone(), None, None, w.global_scale.clone(), w.layout, w.shape)
+                            for w in (w13, w2)))
     x, ids, wts, g13, g2 = batch(wl, args.seed, dev, dense_expert)
     ids_t, wts_t = torch.from_numpy(ids).to(dev), torch.from_numpy(wts).to(dev)
     g13_t, g2_t = torch.from_numpy(g13).to(dev), torch.from_numpy(g2).to(dev)

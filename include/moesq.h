@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define MOESQ_ABI_VERSION 1
+#define MOESQ_ABI_VERSION 2
 /* quantization_config marker "paired48_sparse": {"layout": "pair-bitmask", "version": 1} */
 #define MOESQ_PAIR_BITMASK_VERSION 1
 
@@ -53,18 +53,32 @@ typedef enum { MOESQ_BF16 = 0, MOESQ_F32 = 1 } moesq_dtype;
 /* moe_ffn flags */
 #define MOESQ_FLAG_SYNC_CHECK 1u    /* synchronize the stream before returning and report kernel errors */
 
-/* Weights of one linear of every expert, in pair-bitmask storage. Host struct, read during the call
- * only; its pointers are device memory. Expert e's tensors start at e * N * (K/4), e * N * (K/16),
- * e * N * (K/32) and e * G. G = 2 for a fused gate|up linear: rows [0, N/2) are gate_proj and take
- * global[e*2 + 0], rows [N/2, N) are up_proj and take global[e*2 + 1] (gate and up carry separate
- * global scales: model cards "Qwen3.8-Flash-Next-P48NVFP4-MoESQ" and "Qwen3-30B-A3B-P48NVFP4-MoESQ");
- * G = 1 otherwise. Every pointer 16-byte aligned. */
+/* Weight layouts.
+ * MOESQ_LAYOUT_PAIR_BITMASK: the stored tensors packed / mask / scale as above, per expert.
+ * MOESQ_LAYOUT_TILED: the same bytes re-tiled once at load time for the kernels (the model cards
+ *   note that the serving stack rebuilds each layer into "the kernel's own layout" at load time):
+ *   `packed` points to E * (N/16) * (K/256) records of 1408 bytes, ordered [expert][16-row tile]
+ *   [256-K step]. Record lane l (row l % 16 of the tile, 64-K quarter q = l / 16 of the step) holds
+ *   at 16*l the 16 kept bytes of its 64 K (every 4 bytes = two chunks (b0 b1)(b0' b1') rewritten as
+ *   (lo b0 | lo b1 << 4, hi b0 | hi b1 << 4, lo b0' | lo b1' << 4, hi b0' | hi b1' << 4)), at
+ *   1024 + 4*l its 4 mask bytes and at 1280 + 2*l its 2 scale bytes. mask and scale are unused (NULL).
+ *   Requires K % 256 == 0 and N % 16 == 0; moesq_prepare_weights / moesq_unprepare_weights convert. */
+#define MOESQ_LAYOUT_PAIR_BITMASK 0
+#define MOESQ_LAYOUT_TILED 1
+
+/* Weights of one linear of every expert. Host struct, read during the call only; its pointers are
+ * device memory. Pair-bitmask layout: expert e's tensors start at e * N * (K/4), e * N * (K/16) and
+ * e * N * (K/32). global [E][G]: G = 2 for a fused gate|up linear: rows [0, N/2) are gate_proj and
+ * take global[e*2 + 0], rows [N/2, N) are up_proj and take global[e*2 + 1] (gate and up carry
+ * separate global scales: model cards "Qwen3.8-Flash-Next-P48NVFP4-MoESQ" and
+ * "Qwen3-30B-A3B-P48NVFP4-MoESQ"); G = 1 otherwise. Every pointer 16-byte aligned. */
 typedef struct {
-  const uint8_t *packed;   /* [E][N][K/4]  */
-  const uint8_t *mask;     /* [E][N][K/16] */
-  const uint8_t *scale;    /* [E][N][K/32] */
+  const uint8_t *packed;   /* [E][N][K/4], or the tiled records */
+  const uint8_t *mask;     /* [E][N][K/16] (pair-bitmask layout only) */
+  const uint8_t *scale;    /* [E][N][K/32] (pair-bitmask layout only) */
   const float *global;     /* [E][G]       */
   int32_t E, N, K, G;
+  int32_t layout;          /* MOESQ_LAYOUT_* */
 } moesq_weights;
 
 int moesq_abi_version(void);
@@ -149,6 +163,14 @@ moesq_status moesq_set_stage_events(hipEvent_t *events /* host */, int32_t n);
  * and the mask names the kept pairs. global: 1 float out. K % 32 == 0. */
 moesq_status moesq_compress_weights(const float *w, int64_t N, int32_t K, uint8_t *packed, uint8_t *mask,
                                     uint8_t *scale, float *global, hipStream_t stream);
+
+/* Load-time re-tiling of pair-bitmask weights into MOESQ_LAYOUT_TILED and back (a permutation of
+ * the same bytes, lossless both ways). src: a pair-bitmask moesq_weights (global is not touched);
+ * tiled: moesq_tiled_bytes(E, N, K) bytes out (in). K % 256 == 0, N % 16 == 0. */
+size_t moesq_tiled_bytes(int32_t E, int32_t N, int32_t K);
+moesq_status moesq_prepare_weights(const moesq_weights *src /* host struct */, uint8_t *tiled, hipStream_t stream);
+moesq_status moesq_unprepare_weights(const uint8_t *tiled, int32_t E, int32_t N, int32_t K, uint8_t *packed,
+                                     uint8_t *mask, uint8_t *scale, hipStream_t stream);
 
 /* Storage codec on whole tensors of `rows` rows of K (model card "Sparse storage layout": the encoding
  * is lossless).

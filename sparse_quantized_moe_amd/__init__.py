@@ -32,7 +32,8 @@ EXPORTED_SYMBOLS = (
     "moesq_abi_version", "moesq_status_string", "moesq_last_error", "moesq_quantize_act", "moesq_permute",
     "moesq_grouped_gemm_workspace_size", "moesq_grouped_gemm", "moesq_moe_ffn_layout",
     "moesq_moe_ffn_workspace_size", "moesq_moe_ffn", "moesq_compress_weights", "moesq_validate_weights",
-    "moesq_unpack_pair_bitmask", "moesq_pack_pair_bitmask", "moesq_set_stage_events",
+    "moesq_unpack_pair_bitmask", "moesq_pack_pair_bitmask", "moesq_set_stage_events", "moesq_tiled_bytes",
+    "moesq_prepare_weights", "moesq_unprepare_weights",
 )
 
 
@@ -43,7 +44,11 @@ class MoesqError(RuntimeError):
 class _CWeights(ctypes.Structure):
     _fields_ = [("packed", ctypes.c_void_p), ("mask", ctypes.c_void_p), ("scale", ctypes.c_void_p),
                 ("global_", ctypes.c_void_p), ("E", ctypes.c_int32), ("N", ctypes.c_int32),
-                ("K", ctypes.c_int32), ("G", ctypes.c_int32)]
+                ("K", ctypes.c_int32), ("G", ctypes.c_int32), ("layout", ctypes.c_int32)]
+
+
+LAYOUT_PAIR_BITMASK = 0
+LAYOUT_TILED = 1
 
 
 class _CLayout(ctypes.Structure):
@@ -74,6 +79,9 @@ def _declare(L: ctypes.CDLL) -> None:
         "moesq_unpack_pair_bitmask": (ctypes.c_int, [_P, _P, _I64, _I32, _P, _P, _P]),
         "moesq_pack_pair_bitmask": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _P, _P]),
         "moesq_set_stage_events": (ctypes.c_int, [_P, _I32]),
+        "moesq_tiled_bytes": (_SZ, [_I32, _I32, _I32]),
+        "moesq_prepare_weights": (ctypes.c_int, [ctypes.POINTER(_CWeights), _P, _P]),
+        "moesq_unprepare_weights": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _P, _P, _P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -119,23 +127,30 @@ def _stream() -> int:
 
 @dataclasses.dataclass
 class SparseWeights:
-    """One linear of every expert in pair-bitmask storage (device tensors)."""
-    packed: torch.Tensor        # uint8 [E, N, K/4]
-    mask: torch.Tensor          # uint8 [E, N, K/16]
-    scale: torch.Tensor         # uint8 [E, N, K/32]   (E4M3 bits)
+    """One linear of every expert (device tensors).
+
+    Pair-bitmask layout: ``packed`` u8 [E, N, K/4], ``mask`` u8 [E, N, K/16], ``scale`` u8 [E, N, K/32].
+    Tiled layout (``layout=LAYOUT_TILED``, from ``prepare_weights``): ``packed`` holds the kernel
+    records, ``mask``/``scale`` are None and ``shape`` gives (E, N, K).
+    """
+    packed: torch.Tensor
+    mask: Optional[torch.Tensor]
+    scale: Optional[torch.Tensor]
     global_scale: torch.Tensor  # float32 [E, G]
+    layout: int = LAYOUT_PAIR_BITMASK
+    shape: Optional[tuple] = None
 
     @property
     def E(self) -> int:
-        return self.packed.shape[0]
+        return self.shape[0] if self.shape else self.packed.shape[0]
 
     @property
     def N(self) -> int:
-        return self.packed.shape[1]
+        return self.shape[1] if self.shape else self.packed.shape[1]
 
     @property
     def K(self) -> int:
-        return self.packed.shape[2] * 4
+        return self.shape[2] if self.shape else self.packed.shape[2] * 4
 
     @property
     def G(self) -> int:
@@ -143,14 +158,48 @@ class SparseWeights:
 
     def c_struct(self) -> _CWeights:
         E, N, K = self.E, self.N, self.K
+        if self.layout == LAYOUT_TILED:
+            if self.packed.numel() != lib().moesq_tiled_bytes(E, N, K):
+                raise MoesqError("tiled buffer size does not match (E, N, K)")
+            return _CWeights(_dev(self.packed, "packed", torch.uint8), None, None,
+                             _dev(self.global_scale, "global_scale", torch.float32), E, N, K, self.G, LAYOUT_TILED)
         if tuple(self.mask.shape) != (E, N, K // 16) or tuple(self.scale.shape) != (E, N, K // 32):
             raise MoesqError("mask/scale shapes do not match packed")
         return _CWeights(_dev(self.packed, "packed", torch.uint8), _dev(self.mask, "mask", torch.uint8),
                          _dev(self.scale, "scale", torch.uint8),
-                         _dev(self.global_scale, "global_scale", torch.float32), E, N, K, self.G)
+                         _dev(self.global_scale, "global_scale", torch.float32), E, N, K, self.G,
+                         LAYOUT_PAIR_BITMASK)
 
     def nbytes(self) -> int:
-        return sum(t.numel() * t.element_size() for t in (self.packed, self.mask, self.scale, self.global_scale))
+        ts = [t for t in (self.packed, self.mask, self.scale, self.global_scale) if t is not None]
+        return sum(t.numel() * t.element_size() for t in ts)
+
+
+def prepare_weights(w: SparseWeights) -> SparseWeights:
+    """Load-time re-tiling of pair-bitmask weights into the kernels' layout (the same bytes)."""
+    E, N, K = w.E, w.N, w.K
+    n = lib().moesq_tiled_bytes(E, N, K)
+    if n == 0:
+        raise MoesqError("the tiled layout needs N % 16 == 0 and K % 256 == 0")
+    tiled = torch.empty(n, dtype=torch.uint8, device=w.packed.device)
+    cw = w.c_struct()
+    _check(lib().moesq_prepare_weights(ctypes.byref(cw), _dev(tiled, "tiled"), _stream()))
+    return SparseWeights(tiled, None, None, w.global_scale, LAYOUT_TILED, (E, N, K))
+
+
+def unprepare_weights(w: SparseWeights) -> SparseWeights:
+    """The pair-bitmask tensors back from tiled weights."""
+    E, N, K = w.E, w.N, w.K
+    dev = w.packed.device
+    packed = torch.empty((E, N, K // 4), dtype=torch.uint8, device=dev)
+    mask = torch.empty((E, N, K // 16), dtype=torch.uint8, device=dev)
+    scale = torch.empty((E, N, K // 32), dtype=torch.uint8, device=dev)
+    _check(lib().moesq_unprepare_weights(_dev(w.packed, "tiled", torch.uint8), E, N, K, _dev(packed, "packed"),
+                                         _dev(mask, "mask"), _dev(scale, "scale"), _stream()))
+    return SparseWeights(packed, mask, scale, w.global_scale)
+
+
+__all__ += ["LAYOUT_PAIR_BITMASK", "LAYOUT_TILED", "prepare_weights", "unprepare_weights"]
 
 
 def quantize_act(x: torch.Tensor, global_scale: torch.Tensor, src_row: Optional[torch.Tensor] = None,

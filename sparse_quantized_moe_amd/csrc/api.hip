@@ -36,21 +36,28 @@ size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 moesq_status check_weights(const moesq_weights* w, const char* name) {
   if (!w) return fail(MOESQ_ERR_INVALID, "%s: null weights struct", name);
-  if (!w->packed || !w->mask || !w->scale || !w->global) return fail(MOESQ_ERR_INVALID, "%s: null weight pointer", name);
+  if (w->layout != MOESQ_LAYOUT_PAIR_BITMASK && w->layout != MOESQ_LAYOUT_TILED)
+    return fail(MOESQ_ERR_INVALID, "%s: unknown weight layout", name);
+  const bool tiled = w->layout == MOESQ_LAYOUT_TILED;
+  if (!w->packed || !w->global || (!tiled && (!w->mask || !w->scale)))
+    return fail(MOESQ_ERR_INVALID, "%s: null weight pointer", name);
   if (w->E < 1 || w->N < 1 || w->K < 1) return fail(MOESQ_ERR_INVALID, "%s: E, N, K must be positive", name);
   if (w->G != 1 && w->G != 2) return fail(MOESQ_ERR_INVALID, "%s: G must be 1 or 2", name);
   if (w->K % 32) return fail(MOESQ_ERR_INVALID, "%s: K must be a multiple of 32", name);
   if (w->K % 256) return fail(MOESQ_ERR_UNSUPPORTED, "%s: the GEMM needs K % 256 == 0", name);
   if (w->N % 64) return fail(MOESQ_ERR_UNSUPPORTED, "%s: the GEMM needs N % 64 == 0", name);
   if (w->E > 1024) return fail(MOESQ_ERR_UNSUPPORTED, "%s: at most 1024 experts", name);
-  if (!aligned16(w->packed) || !aligned16(w->mask) || !aligned16(w->scale))
+  if (!aligned16(w->packed) || (!tiled && (!aligned16(w->mask) || !aligned16(w->scale))))
     return fail(MOESQ_ERR_INVALID, "%s: weight tensors must be 16-byte aligned", name);
   return MOESQ_OK;
 }
 
-int ffn_tactic(int64_t T, int32_t k, int32_t E) {
-  // mean rows per expert: small batches stream each expert once, large ones reuse weight fragments
-  return (T * k) <= (int64_t)48 * E ? moesq::kTacticDecode : moesq::kTacticPrefill;
+// Small batches (mean rows per expert <= 48) stream each expert's weights once per 32 rows with the
+// activations of the whole K in LDS; large ones tile 128 rows and reuse each decoded weight fragment.
+int ffn_tactic(int64_t rows, int32_t E, int32_t K1, int32_t K2) {
+  const bool fits = moesq::gemm_lds_bytes(moesq::kTacticDecode, K1) <= moesq::kMaxLdsBytes &&
+                    moesq::gemm_lds_bytes(moesq::kTacticDecode, K2) <= moesq::kMaxLdsBytes;
+  return (rows <= (int64_t)48 * E && fits) ? moesq::kTacticDecode : moesq::kTacticPrefill;
 }
 
 }  // namespace
@@ -121,16 +128,17 @@ moesq_status moesq_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
                 "grouped_gemm: null pointer");
   MOESQ_REQUIRE(workspace_bytes >= moesq_grouped_gemm_workspace_size(w->E), MOESQ_ERR_WORKSPACE,
                 "grouped_gemm: workspace too small");
-  MOESQ_REQUIRE(aligned16(out) && aligned16(a_codes), MOESQ_ERR_INVALID, "grouped_gemm: out and a_codes must be 16-byte aligned");
+  MOESQ_REQUIRE(aligned16(out) && aligned16(a_codes) && ((uintptr_t)a_scales & 3) == 0, MOESQ_ERR_INVALID,
+                "grouped_gemm: out and a_codes must be 16-byte aligned, a_scales 4-byte aligned");
   MOESQ_REQUIRE(rows * w->K / 2 < ((int64_t)1 << 40), MOESQ_ERR_UNSUPPORTED, "grouped_gemm: too many rows");
-  const int tactic = ffn_tactic(rows, 1, w->E);
+  const int tactic = ffn_tactic(rows, w->E, w->K, w->K);
   int32_t* tile_offsets = static_cast<int32_t*>(workspace);
   moesq::launch_tile_offsets(expert_offsets, w->E, moesq::tactic_rows_per_mblock(tactic), tile_offsets, stream);
   moesq::GemmParams p{};
   p.a_codes = a_codes; p.a_scales = a_scales; p.a_global = a_global; p.offsets = expert_offsets;
   p.tile_offsets = tile_offsets; p.rows = rows;
   p.w_packed = w->packed; p.w_mask = w->mask; p.w_scale = w->scale; p.w_global = w->global;
-  p.E = w->E; p.N = w->N; p.K = w->K; p.G = w->G; p.out = out;
+  p.E = w->E; p.N = w->N; p.K = w->K; p.G = w->G; p.layout = w->layout; p.out = out;
   moesq::launch_grouped_gemm(p, moesq::kEpiStore, tactic, stream);
   return check_launch(stream, false);
 }
@@ -155,7 +163,7 @@ moesq_status moesq_moe_ffn_layout(int64_t T, int32_t H, int32_t I, int32_t k, in
   L->a2_scales = take(P * (size_t)(I / 32));
   L->down_rows = take(P * (size_t)H * 4);
   L->total = off;
-  L->rows_per_mblock = moesq::tactic_rows_per_mblock(ffn_tactic(T, k, E));
+  L->rows_per_mblock = moesq::tactic_rows_per_mblock(ffn_tactic(T * k, E, H, I));
   return MOESQ_OK;
 }
 
@@ -201,7 +209,7 @@ moesq_status moesq_moe_ffn(const void* x, int64_t T, int32_t H, const int32_t* t
   uint8_t* a2c = ws + L.a2_codes;
   uint8_t* a2s = ws + L.a2_scales;
   float* drows = reinterpret_cast<float*>(ws + L.down_rows);
-  const int tactic = ffn_tactic(T, k, E);
+  const int tactic = ffn_tactic(T * k, E, H, I);
   const int64_t P = T * k;
 
   stage_event(0, stream);
@@ -213,13 +221,13 @@ moesq_status moesq_moe_ffn(const void* x, int64_t T, int32_t H, const int32_t* t
   moesq::GemmParams g{};
   g.a_codes = a13c; g.a_scales = a13s; g.a_global = a13_global; g.offsets = offsets; g.tile_offsets = tile_offsets;
   g.rows = P; g.w_packed = w13->packed; g.w_mask = w13->mask; g.w_scale = w13->scale; g.w_global = w13->global;
-  g.E = E; g.N = w13->N; g.K = H; g.G = 2; g.h_codes = a2c; g.h_scales = a2s; g.h_global = a2_global;
+  g.E = E; g.N = w13->N; g.K = H; g.G = 2; g.layout = w13->layout; g.h_codes = a2c; g.h_scales = a2s; g.h_global = a2_global;
   moesq::launch_grouped_gemm(g, moesq::kEpiGateUp, tactic, stream);
   stage_event(3, stream);
   moesq::GemmParams d{};
   d.a_codes = a2c; d.a_scales = a2s; d.a_global = a2_global; d.offsets = offsets; d.tile_offsets = tile_offsets;
   d.rows = P; d.w_packed = w2->packed; d.w_mask = w2->mask; d.w_scale = w2->scale; d.w_global = w2->global;
-  d.E = E; d.N = H; d.K = I; d.G = 1; d.out = drows; d.topk_weights = topk_weights; d.sorted = sorted;
+  d.E = E; d.N = H; d.K = I; d.G = 1; d.layout = w2->layout; d.out = drows; d.topk_weights = topk_weights; d.sorted = sorted;
   moesq::launch_grouped_gemm(d, moesq::kEpiDown, tactic, stream);
   stage_event(4, stream);
   moesq::launch_combine(drows, inv, T, k, H, out, stream);
@@ -234,6 +242,34 @@ moesq_status moesq_compress_weights(const float* w, int64_t N, int32_t K, uint8_
   MOESQ_REQUIRE(aligned16(w) && ((uintptr_t)packed & 3) == 0 && ((uintptr_t)mask & 1) == 0 && ((uintptr_t)global & 3) == 0,
                 MOESQ_ERR_INVALID, "compress_weights: w 16-byte, packed 4-byte, mask 2-byte aligned");
   moesq::launch_compress(w, N, K, packed, mask, scale, global, stream);
+  return check_launch(stream, false);
+}
+
+size_t moesq_tiled_bytes(int32_t E, int32_t N, int32_t K) {
+  if (E < 1 || N < 16 || K < 256 || N % 16 || K % 256) return 0;
+  return moesq::tiled_bytes(E, N, K);
+}
+
+moesq_status moesq_prepare_weights(const moesq_weights* src, uint8_t* tiled, hipStream_t stream) {
+  MOESQ_REQUIRE(src && tiled, MOESQ_ERR_INVALID, "prepare_weights: null pointer");
+  MOESQ_REQUIRE(src->layout == MOESQ_LAYOUT_PAIR_BITMASK, MOESQ_ERR_INVALID, "prepare_weights: source must be pair-bitmask");
+  MOESQ_REQUIRE(src->packed && src->mask && src->scale, MOESQ_ERR_INVALID, "prepare_weights: null weight pointer");
+  MOESQ_REQUIRE(src->E >= 1 && src->N >= 16 && src->K >= 256, MOESQ_ERR_INVALID, "prepare_weights: bad sizes");
+  MOESQ_REQUIRE(src->N % 16 == 0 && src->K % 256 == 0, MOESQ_ERR_UNSUPPORTED, "prepare_weights: needs N % 16 == 0, K % 256 == 0");
+  MOESQ_REQUIRE(aligned16(src->packed) && ((uintptr_t)src->mask & 3) == 0 && ((uintptr_t)src->scale & 1) == 0 && aligned16(tiled),
+                MOESQ_ERR_INVALID, "prepare_weights: alignment (packed, tiled 16 B; mask 4 B; scale 2 B)");
+  moesq::launch_prepare(src->packed, src->mask, src->scale, src->E, src->N, src->K, tiled, stream);
+  return check_launch(stream, false);
+}
+
+moesq_status moesq_unprepare_weights(const uint8_t* tiled, int32_t E, int32_t N, int32_t K, uint8_t* packed, uint8_t* mask,
+                                     uint8_t* scale, hipStream_t stream) {
+  MOESQ_REQUIRE(tiled && packed && mask && scale, MOESQ_ERR_INVALID, "unprepare_weights: null pointer");
+  MOESQ_REQUIRE(E >= 1 && N >= 16 && K >= 256, MOESQ_ERR_INVALID, "unprepare_weights: bad sizes");
+  MOESQ_REQUIRE(N % 16 == 0 && K % 256 == 0, MOESQ_ERR_UNSUPPORTED, "unprepare_weights: needs N % 16 == 0, K % 256 == 0");
+  MOESQ_REQUIRE(aligned16(packed) && ((uintptr_t)mask & 3) == 0 && ((uintptr_t)scale & 1) == 0 && aligned16(tiled),
+                MOESQ_ERR_INVALID, "unprepare_weights: alignment (packed, tiled 16 B; mask 4 B; scale 2 B)");
+  moesq::launch_unprepare(tiled, E, N, K, packed, mask, scale, stream);
   return check_launch(stream, false);
 }
 

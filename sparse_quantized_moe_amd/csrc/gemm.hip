@@ -13,155 +13,229 @@
 // of two such values are exact in fp32 and accumulation is in fp32. Global scales are applied in the
 // fp32 epilogue.
 //
-// Work decomposition (one workgroup = 4 waves):
-//   * a workgroup owns one m-block (up to TG*16 rows of one expert) and one n-block (256 weight rows;
-//     for the fused gate|up epilogue 128 intermediate columns = their 128 gate and 128 up rows);
-//   * each wave owns 4 row-tiles of 16 weight rows and streams their kept bytes, masks and scales
-//     straight from HBM into registers (16 B + 4 B + 2 B per lane per 256 K, one load each),
-//     prefetching the next 256 K while the current one is in the MFMAs;
-//   * the m-block's activations are dequantized once per K-chunk into LDS in the B-operand order.
-// Per 256 K a lane holds the contiguous 64 K [64 q, 64 q + 64) of its row (q = lane / 16); smfmac t
-// (t = 0..3) takes chunks 2t, 2t+1 of it. The B lanes read the matching chunks from LDS.
+// Lane data per 256-K super-step: lane (row = lane % 16, q = lane / 16) of a row-tile holds the 64
+// contiguous K [64 q, 64 q + 64) of its weight row (16 B kept bytes, 4 B masks, 2 B scales; one load
+// each), and smfmac t (t = 0..3) uses chunks 2t, 2t+1 of it. The sparse operand's lane q covers the
+// MFMA's 8-K chunk positions {c0(q), c0(q) + 2} with c0 = 0, 4, 1, 5 for q = 0..3, so B lane qb must
+// hold the local chunks 8*(qb/2) + 2t + (qb%2) and that + 16.
 //
-// Tactics: "decode" (TG = 2: 32 rows per m-block, K-chunk 1024) streams each expert's weights once
-// for small batches; "prefill" (TG = 8: 128 rows, K-chunk 256) reuses each decoded weight fragment
-// over 8 token tiles.
-#include "moesq_device.h"
-#include "moesq_internal.h"
+// Two kernels:
+//   * k_gemm_decode (small batches): a workgroup owns one m-block (<= 32 rows of one expert) and
+//     256 weight rows; its activations are staged in LDS as exact f16 in the B-operand order (32 KB
+//     at a time). Weights stream from HBM straight into registers, two super-steps ahead.
+//   * k_gemm_prefill (large batches): a workgroup owns 128 rows x 256 weight rows; per 256-K step it
+//     dequantizes the activations into LDS as f16 and each wave reuses every decoded weight fragment
+//     over 8 token tiles.
+#include "gemm_common.h"
 
 namespace moesq {
 
 constexpr int kGemmThreads = 256;
 
-template <int TG, int KC>
-struct GemmShape {
-  static constexpr int BMT = TG * 16;                 // rows (tokens) per m-block
-  static constexpr int ROW_STRIDE = KC * 2 + 16;      // bytes per token row in LDS (+16 B skew)
-  static constexpr int LDS_B = BMT * ROW_STRIDE;
-};
+// ---------------------------------------------------------------------------------------------
+// Decode kernel
+// ---------------------------------------------------------------------------------------------
+constexpr int kDecLdsB = 32 * 1024;           // activation bytes staged in LDS at a time
 
-template <int EPI, int TG, int KC>
-__global__ __launch_bounds__(kGemmThreads) void k_grouped_gemm(GemmParams p) {
-  using S = GemmShape<TG, KC>;
+// K staged per chunk for TG token tiles (a multiple of 256).
+__host__ __device__ constexpr int dec_kc(int TG) { return kDecLdsB / (TG * 16 * 2); }
+
+// Position of local chunk c (0..31) of a super-step in LDS: c and c+16 sit side by side, so a B
+// lane's two chunks are one contiguous 32-byte read.
+__device__ __forceinline__ int dec_chunk_pos(int c) { return ((c & 15) << 1) | (c >> 4); }
+
+template <int EPI, int LAYOUT, int TG>
+__global__ __launch_bounds__(kGemmThreads) void k_gemm_decode(GemmParams p) {
+  constexpr int BMT = TG * 16;
+  constexpr int KCMAX = dec_kc(TG);
+  constexpr int RS = KCMAX * 2 + 16;                              // LDS bytes per token row (+16 B skew)
   extern __shared__ __align__(16) uint8_t smem[];
-  uint8_t* sB = smem;
-  uint16_t* lut = reinterpret_cast<uint16_t*>(smem + S::LDS_B);
   __shared__ int s_e;
+  const int K = p.K;
+  uint8_t* sB = smem;                                             // [BMT][RS] f16, chunk pairs adjacent
+  uint16_t* lut_idx = reinterpret_cast<uint16_t*>(smem + BMT * RS);   // [256]
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int mb = blockIdx.x, nb = blockIdx.y;
-  const int E = p.E, N = p.N, K = p.K;
-
-  if (tid == 0) s_e = -1;
-  __syncthreads();
-  for (int e = tid; e < E; e += kGemmThreads) {
-    const int a = p.tile_offsets[e], b = p.tile_offsets[e + 1];
-    if (a <= mb && mb < b) s_e = e;
-  }
-  lut[tid] = (uint16_t)smfmac_index_of_mask_byte((uint32_t)tid);
-  __syncthreads();
-  const int e = s_e;
+  lut_idx[tid] = (uint16_t)smfmac_index_of_mask_byte((uint32_t)tid);
+  const int e = find_expert(p.tile_offsets, p.E, mb, &s_e);
   if (e < 0) return;
   const int row0 = p.offsets[e];
   const int M = p.offsets[e + 1] - row0;
-  const int m0 = (mb - p.tile_offsets[e]) * S::BMT;
-  const int mrows = M - m0 < S::BMT ? M - m0 : S::BMT;
+  const int m0 = (mb - p.tile_offsets[e]) * BMT;
+  const int mrows = M - m0 < BMT ? M - m0 : BMT;
+  const int ntiles = (mrows + 15) >> 4;
 
-  // weight rows of this wave
   int wrow[4];
-  bool active;
-  if (EPI == kEpiGateUp) {
-    const int I = N >> 1;
-    const int hcol0 = nb * 128 + wv * 32;
-    active = hcol0 < I;
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) wrow[rt] = (rt < 2 ? 0 : I) + hcol0 + (rt & 1) * 16;
-  } else {
-    const int r0 = nb * 256 + wv * 64;
-    active = r0 < N;
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) wrow[rt] = r0 + rt * 16;
+  const bool active = wave_rows<EPI>(p.N, nb, wv, wrow);
+  WeightPtrs<LAYOUT> wp;
+  wp.init(p, e, wrow, active, lane);
+  const int nsteps = K >> 8;
+  constexpr int spc = KCMAX >> 8;                                 // super-steps per staged chunk
+  WeightFrag w0, w1, w2;
+  if (active) {
+    wp.load(0, w0);
+    if (nsteps > 1) wp.load(1, w1);
   }
-  const int qa = lane >> 4;
-  const uint8_t* pk_ptr[4];
-  const uint8_t* mk_ptr[4];
-  const uint8_t* sc_ptr[4];
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    const int64_t wr = (int64_t)e * N + (active ? wrow[rt] + (lane & 15) : 0);
-    pk_ptr[rt] = p.w_packed + wr * (K >> 2) + 16 * qa;
-    mk_ptr[rt] = p.w_mask + wr * (K >> 4) + 4 * qa;
-    sc_ptr[rt] = p.w_scale + wr * (K >> 5) + 2 * qa;
-  }
-
   f32x4 acc[4][TG];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
     for (int tt = 0; tt < TG; ++tt) acc[rt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nsteps = K >> 8;
-  constexpr int SPC = KC / 256;          // super-steps per K-chunk
-  u32x4 pk[4];
-  uint32_t mk[4], sc[4];
-  if (active) {
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      pk[rt] = *reinterpret_cast<const u32x4*>(pk_ptr[rt]);
-      mk[rt] = *reinterpret_cast<const uint32_t*>(mk_ptr[rt]);
-      sc[rt] = *reinterpret_cast<const uint16_t*>(sc_ptr[rt]);
-    }
-  }
-  const int64_t a_row_bytes = K >> 1, a_row_scales = K >> 5;
-  for (int gs = 0; gs < nsteps; ++gs) {
-    const int ssl = gs % SPC;
+  const int nrow = lane & 15, qb = lane >> 4;
+  const int64_t arow = (int64_t)(row0 + m0) * (K >> 1);
+  const int64_t srow = (int64_t)(row0 + m0) * (K >> 5);
+  auto step = [&](int gs, const WeightFrag& w) {
+    const int ssl = gs % spc;
     if (ssl == 0) {
+      // stage the K-chunk [k0, k0 + kc) of the m-block's activations as exact f16
       const int k0 = gs * 256;
-      const int kc = K - k0 < KC ? K - k0 : KC;
-      const int cpr = kc >> 3;               // chunks per row in this K-chunk
+      const int kc = K - k0 < KCMAX ? K - k0 : KCMAX;
+      const int quads = kc >> 5;                                  // 4-chunk groups (32 K) per row
       __syncthreads();
-      for (int i = tid; i < S::BMT * cpr; i += kGemmThreads) {
-        const int n = i / cpr, c = i - n * cpr;
+      for (int i = tid; i < ntiles * 16 * quads; i += kGemmThreads) {
+        const int n = i / quads, q4 = i - n * quads;
         u32x4 v = u32x4{0u, 0u, 0u, 0u};
+        uint32_t sb = 0;
         if (n < mrows) {
-          const int64_t ar = row0 + m0 + n;
-          const uint32_t codes = *reinterpret_cast<const uint32_t*>(p.a_codes + ar * a_row_bytes + ((k0 >> 3) + c) * 4);
-          const uint32_t sb = p.a_scales[ar * a_row_scales + ((k0 + 8 * c) >> 5)];
-          const f16 s = e4m3_to_f16(sb);
-          v = act_chunk_kprime(codes, f16x2{s, s});
+          v = *reinterpret_cast<const u32x4*>(p.a_codes + arow + (int64_t)n * (K >> 1) + (k0 >> 1) + q4 * 16);
+          sb = p.a_scales[srow + (int64_t)n * (K >> 5) + (k0 >> 5) + q4];
         }
-        *reinterpret_cast<u32x4*>(sB + n * S::ROW_STRIDE + c * 16) = v;
+        const f16 s = e4m3_to_f16(sb);
+        const f16x2 s2 = f16x2{s, s};
+        const uint32_t wv4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int c = 4 * q4 + j;                               // chunk within the staged K-chunk
+          const int pos = (c & ~31) + dec_chunk_pos(c & 31);
+          *reinterpret_cast<u32x4*>(sB + n * RS + pos * 16) = act_chunk_kprime(wv4[j], s2);
+        }
       }
       __syncthreads();
     }
-    u32x4 pk_n[4];
-    uint32_t mk_n[4], sc_n[4];
-    if (active && gs + 1 < nsteps) {
+    if (!active) return;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      f16x8 A[4];
+      int idx[4];
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        pk_n[rt] = *reinterpret_cast<const u32x4*>(pk_ptr[rt] + 64 * (gs + 1));
-        mk_n[rt] = *reinterpret_cast<const uint32_t*>(mk_ptr[rt] + 16 * (gs + 1));
-        sc_n[rt] = *reinterpret_cast<const uint16_t*>(sc_ptr[rt] + 8 * (gs + 1));
+        const f16x2 sp = scale_pair_f16(w.sc[rt]);
+        const f16x2 s2 = (t < 2) ? __builtin_shufflevector(sp, sp, 0, 0) : __builtin_shufflevector(sp, sp, 1, 1);
+        A[rt] = weight_operand_of<LAYOUT>(frag_word(w.pk[rt], t), s2);
+        idx[rt] = lut_idx[(w.mk[rt] >> (8 * t)) & 255u];
+      }
+      const int c0 = 8 * (qb >> 1) + 2 * t + (qb & 1);
+#pragma unroll
+      for (int tt = 0; tt < TG; ++tt) {
+        if (tt < ntiles) {
+          const uint8_t* bp = sB + (tt * 16 + nrow) * RS + (32 * ssl + 2 * c0) * 16;
+          const u32x4 b0 = *reinterpret_cast<const u32x4*>(bp);
+          const u32x4 b1 = *reinterpret_cast<const u32x4*>(bp + 16);
+          const f16x16 B = __builtin_bit_cast(f16x16, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt)
+            acc[rt][tt] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(A[rt], B, acc[rt][tt], idx[rt], 0, 0);
+        }
       }
     }
+  };
+  // Three-slot register ring, unrolled by its period so no register of a load in flight is ever
+  // copied: step gs reads slot gs % 3 while the loads of gs + 1 and gs + 2 are outstanding.
+  int gs = 0;
+  for (; gs + 3 <= nsteps; gs += 3) {
+    if (active && gs + 2 < nsteps) wp.load(gs + 2, w2);
+    step(gs, w0);
+    if (active && gs + 3 < nsteps) wp.load(gs + 3, w0);
+    step(gs + 1, w1);
+    if (active && gs + 4 < nsteps) wp.load(gs + 4, w1);
+    step(gs + 2, w2);
+  }
+  if (gs < nsteps) step(gs, w0);
+  if (gs + 1 < nsteps) step(gs + 1, w1);
+  if (!active) return;
+  gemm_epilogue<EPI, TG>(p, acc, e, row0, m0, mrows, nb, wv, wrow, lane);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Prefill kernel
+// ---------------------------------------------------------------------------------------------
+constexpr int kPreTG = 8;
+constexpr int kPreBMT = kPreTG * 16;
+constexpr int kPreRowStride = 256 * 2 + 16;   // bytes per token row of one 256-K step in LDS (+16 B skew)
+constexpr int kPreLdsB = kPreBMT * kPreRowStride;
+
+template <int EPI, int LAYOUT>
+__global__ __launch_bounds__(kGemmThreads) void k_gemm_prefill(GemmParams p) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint8_t* sB = smem;
+  uint16_t* lut = reinterpret_cast<uint16_t*>(smem + kPreLdsB);
+  __shared__ int s_e;
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int mb = blockIdx.x, nb = blockIdx.y;
+  const int K = p.K;
+  lut[tid] = (uint16_t)smfmac_index_of_mask_byte((uint32_t)tid);
+  const int e = find_expert(p.tile_offsets, p.E, mb, &s_e);
+  if (e < 0) return;
+  const int row0 = p.offsets[e];
+  const int M = p.offsets[e + 1] - row0;
+  const int m0 = (mb - p.tile_offsets[e]) * kPreBMT;
+  const int mrows = M - m0 < kPreBMT ? M - m0 : kPreBMT;
+
+  int wrow[4];
+  const bool active = wave_rows<EPI>(p.N, nb, wv, wrow);
+  WeightPtrs<LAYOUT> wp;
+  wp.init(p, e, wrow, active, lane);
+
+  f32x4 acc[4][kPreTG];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int tt = 0; tt < kPreTG; ++tt) acc[rt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nsteps = K >> 8;
+  WeightFrag wa, wb;
+  if (active) wp.load(0, wa);
+  const int64_t a_row_bytes = K >> 1, a_row_scales = K >> 5;
+  // one 256-K step: stage the activations of this K range into LDS, prefetch the next weight
+  // fragment into `nxt`, run the MFMAs on `cur`
+  auto step = [&](int gs, const WeightFrag& cur, WeightFrag& nxt) {
+    const int k0 = gs * 256;
+    __syncthreads();
+    for (int i = tid; i < kPreBMT * 32; i += kGemmThreads) {
+      const int n = i >> 5, c = i & 31;
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (n < mrows) {
+        const int64_t ar = row0 + m0 + n;
+        const uint32_t codes = *reinterpret_cast<const uint32_t*>(p.a_codes + ar * a_row_bytes + ((k0 >> 3) + c) * 4);
+        const uint32_t sb = p.a_scales[ar * a_row_scales + ((k0 >> 5) + (c >> 2))];
+        const f16 s = e4m3_to_f16(sb);
+        v = act_chunk_kprime(codes, f16x2{s, s});
+      }
+      *reinterpret_cast<u32x4*>(sB + n * kPreRowStride + c * 16) = v;
+    }
+    __syncthreads();
+    if (active && gs + 1 < nsteps) wp.load(gs + 1, nxt);
     if (active) {
       const int nrow = lane & 15, qb = lane >> 4;
-      const uint8_t* brow = sB + nrow * S::ROW_STRIDE + (32 * ssl + 8 * (qb >> 1) + (qb & 1)) * 16;
+      const uint8_t* brow = sB + nrow * kPreRowStride + (8 * (qb >> 1) + (qb & 1)) * 16;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         f16x8 A[4];
         int idx[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-          const uint32_t kept = t == 0 ? pk[rt].x : t == 1 ? pk[rt].y : t == 2 ? pk[rt].z : pk[rt].w;
-          const f16 s = e4m3_to_f16((sc[rt] >> (8 * (t >> 1))) & 255u);
-          A[rt] = weight_operand(kept, f16x2{s, s});
-          idx[rt] = lut[(mk[rt] >> (8 * t)) & 255u];
+          const f16x2 sp = scale_pair_f16(cur.sc[rt]);
+          const f16x2 s2 = (t < 2) ? __builtin_shufflevector(sp, sp, 0, 0) : __builtin_shufflevector(sp, sp, 1, 1);
+          A[rt] = weight_operand_of<LAYOUT>(frag_word(cur.pk[rt], t), s2);
+          idx[rt] = lut[(cur.mk[rt] >> (8 * t)) & 255u];
         }
 #pragma unroll
-        for (int tt = 0; tt < TG; ++tt) {
+        for (int tt = 0; tt < kPreTG; ++tt) {
           if (tt * 16 < mrows) {
-            const uint8_t* bp = brow + tt * 16 * S::ROW_STRIDE + 2 * t * 16;
+            const uint8_t* bp = brow + tt * 16 * kPreRowStride + 2 * t * 16;
             const u32x4 b0 = *reinterpret_cast<const u32x4*>(bp);
             const u32x4 b1 = *reinterpret_cast<const u32x4*>(bp + 16 * 16);
             const f16x16 B = __builtin_bit_cast(f16x16, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -172,104 +246,67 @@ __global__ __launch_bounds__(kGemmThreads) void k_grouped_gemm(GemmParams p) {
         }
       }
     }
-    if (active && gs + 1 < nsteps) {
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) { pk[rt] = pk_n[rt]; mk[rt] = mk_n[rt]; sc[rt] = sc_n[rt]; }
-    }
+  };
+  int gs = 0;
+  for (; gs + 2 <= nsteps; gs += 2) {
+    step(gs, wa, wb);
+    step(gs + 1, wb, wa);
   }
+  if (gs < nsteps) step(gs, wa, wb);
   if (!active) return;
+  gemm_epilogue<EPI, kPreTG>(p, acc, e, row0, m0, mrows, nb, wv, wrow, lane);
+}
 
-  // ---- epilogues ----
-  const int ntok = lane & 15;
-  const float ag = p.a_global[e];
-  if (EPI == kEpiGateUp) {
-    const int I = N >> 1;
-    const int hcol0 = nb * 128 + wv * 32;
-    const float g_gate = ag * p.w_global[2 * e];
-    const float g_up = ag * p.w_global[2 * e + 1];
-    const float g2 = p.h_global[e];
-#pragma unroll
-    for (int tt = 0; tt < TG; ++tt) {
-      if (tt * 16 >= mrows) continue;
-      const int n = tt * 16 + ntok;
-      float h[2][4];
-      float amax = 0.0f;
-#pragma unroll
-      for (int half = 0; half < 2; ++half)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float gt = acc[half][tt][r] * g_gate;
-          const float up = acc[2 + half][tt][r] * g_up;
-          const float hv = gt / (1.0f + __expf(-gt)) * up;
-          h[half][r] = hv;
-          amax = __builtin_fmaxf(amax, __builtin_fabsf(hv));
-        }
-      amax = __builtin_fmaxf(amax, __shfl_xor(amax, 16));
-      amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32));
-      const int scb = scale_code(amax, g2);
-      const float s = e4m3_value(scb);
-      if (n < mrows) {
-        const int64_t row = row0 + m0 + n;
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const uint32_t c0 = nvfp4_code(h[half][0], s, g2), c1 = nvfp4_code(h[half][1], s, g2);
-          const uint32_t c2 = nvfp4_code(h[half][2], s, g2), c3 = nvfp4_code(h[half][3], s, g2);
-          const uint16_t v = (uint16_t)(c0 | (c1 << 4) | (c2 << 8) | (c3 << 12));
-          *reinterpret_cast<uint16_t*>(p.h_codes + row * (I >> 1) + ((hcol0 + half * 16 + 4 * qa) >> 1)) = v;
-        }
-        if (qa == 0) p.h_scales[row * (I >> 5) + (hcol0 >> 5)] = (uint8_t)scb;
-      }
-    }
-  } else {
-#pragma unroll
-    for (int tt = 0; tt < TG; ++tt) {
-      if (tt * 16 >= mrows) continue;
-      const int n = tt * 16 + ntok;
-      if (n >= mrows) continue;
-      const int64_t row = row0 + m0 + n;
-      float gsc;
-      if (EPI == kEpiDown) gsc = ag * p.w_global[e] * p.topk_weights[p.sorted[row]];
-      else gsc = ag;
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        const int col = wrow[rt] + 4 * qa;
-        float gcol = gsc;
-        if (EPI == kEpiStore) gcol = gsc * (p.G == 2 ? p.w_global[2 * e + (col >= (N >> 1) ? 1 : 0)] : p.w_global[e]);
-        const f32x4 v = acc[rt][tt] * gcol;
-        *reinterpret_cast<f32x4*>(p.out + row * N + col) = v;
-      }
-    }
+constexpr int kDecTG = 2;                     // token tiles per decode m-block
+
+int tactic_rows_per_mblock(int tactic) { return tactic == kTacticPrefill ? kPreBMT : kDecTG * 16; }
+
+size_t gemm_lds_bytes(int tactic, int K) {
+  (void)K;
+  return tactic == kTacticPrefill ? (size_t)kPreLdsB + 512 : (size_t)kDecTG * 16 * (dec_kc(kDecTG) * 2 + 16) + 512;
+}
+
+template <class Kern>
+static void set_lds_attr(Kern* k, size_t lds) {
+  static size_t done = 0;   // largest size already granted for this kernel
+  if (lds > done) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    done = lds;
   }
 }
 
-int tactic_rows_per_mblock(int tactic) { return tactic == kTacticPrefill ? 128 : 32; }
-
-template <int EPI, int TG, int KC>
-static void launch_variant(const GemmParams& p, hipStream_t stream) {
-  using S = GemmShape<TG, KC>;
-  const size_t lds = S::LDS_B + 512;
-  static bool attr = false;
-  if (!attr) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_grouped_gemm<EPI, TG, KC>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    attr = true;
-  }
-  const int64_t mblocks = (p.rows + S::BMT - 1) / S::BMT + p.E;
+template <int EPI, int LAYOUT>
+static void launch_decode(const GemmParams& p, hipStream_t stream) {
+  const size_t lds = gemm_lds_bytes(kTacticDecode, p.K);
+  set_lds_attr(&k_gemm_decode<EPI, LAYOUT, kDecTG>, lds);
+  const int64_t mblocks = (p.rows + kDecTG * 16 - 1) / (kDecTG * 16) + p.E;
   const int nblocks = EPI == kEpiGateUp ? ((p.N >> 1) + 127) / 128 : (p.N + 255) / 256;
-  if (mblocks <= 0 || nblocks <= 0) return;
-  k_grouped_gemm<EPI, TG, KC><<<dim3((unsigned)mblocks, (unsigned)nblocks), kGemmThreads, lds, stream>>>(p);
+  k_gemm_decode<EPI, LAYOUT, kDecTG><<<dim3((unsigned)mblocks, (unsigned)nblocks), kGemmThreads, lds, stream>>>(p);
+}
+
+template <int EPI, int LAYOUT>
+static void launch_prefill(const GemmParams& p, hipStream_t stream) {
+  const size_t lds = gemm_lds_bytes(kTacticPrefill, p.K);
+  set_lds_attr(&k_gemm_prefill<EPI, LAYOUT>, lds);
+  const int64_t mblocks = (p.rows + kPreBMT - 1) / kPreBMT + p.E;
+  const int nblocks = EPI == kEpiGateUp ? ((p.N >> 1) + 127) / 128 : (p.N + 255) / 256;
+  k_gemm_prefill<EPI, LAYOUT><<<dim3((unsigned)mblocks, (unsigned)nblocks), kGemmThreads, lds, stream>>>(p);
+}
+
+template <int EPI>
+static void launch_epi(const GemmParams& p, int tactic, hipStream_t stream) {
+  if (tactic == kTacticPrefill) {
+    if (p.layout == 1) launch_prefill<EPI, 1>(p, stream); else launch_prefill<EPI, 0>(p, stream);
+  } else {
+    if (p.layout == 1) launch_decode<EPI, 1>(p, stream); else launch_decode<EPI, 0>(p, stream);
+  }
 }
 
 void launch_grouped_gemm(const GemmParams& p, int epi, int tactic, hipStream_t stream) {
-  if (tactic == kTacticPrefill) {
-    if (epi == kEpiStore) launch_variant<kEpiStore, 8, 256>(p, stream);
-    else if (epi == kEpiGateUp) launch_variant<kEpiGateUp, 8, 256>(p, stream);
-    else launch_variant<kEpiDown, 8, 256>(p, stream);
-  } else {
-    if (epi == kEpiStore) launch_variant<kEpiStore, 2, 1024>(p, stream);
-    else if (epi == kEpiGateUp) launch_variant<kEpiGateUp, 2, 1024>(p, stream);
-    else launch_variant<kEpiDown, 2, 1024>(p, stream);
-  }
+  if (p.rows <= 0) return;
+  if (epi == kEpiStore) launch_epi<kEpiStore>(p, tactic, stream);
+  else if (epi == kEpiGateUp) launch_epi<kEpiGateUp>(p, tactic, stream);
+  else launch_epi<kEpiDown>(p, tactic, stream);
 }
 
 // ---------------------------------------------------------------------------------------------

@@ -1,0 +1,168 @@
+// Pieces shared by the grouped sparse GEMM kernels: block -> (expert, m-block) lookup, per-lane
+// weight fragments of the pair-bitmask storage, and the three epilogues.
+#pragma once
+#include "moesq_device.h"
+#include "moesq_internal.h"
+
+namespace moesq {
+
+// Kept bytes, masks and scales one lane needs for one 256-K super-step of 4 row-tiles: 16 B of
+// packed, 4 B of mask and 2 B of scale per row-tile (the lane's 64 contiguous K of its row).
+struct WeightFrag {
+  u32x4 pk[4];
+  uint32_t mk[4];
+  uint32_t sc[4];
+};
+
+// LAYOUT 0: pair-bitmask storage (three row-major tensors); LAYOUT 1: tiled records, one
+// contiguous 1408-byte record per (16-row tile, 256-K step), so each load of a wave is coalesced.
+template <int LAYOUT>
+struct WeightPtrs {
+  const uint8_t* pk[4];
+  const uint8_t* mk[4];
+  const uint8_t* sc[4];
+  int64_t step;   // bytes between consecutive 256-K steps of the packed pointer
+
+  __device__ __forceinline__ void init(const GemmParams& p, int e, const int wrow[4], bool active, int lane) {
+    const int K = p.K, qa = lane >> 4;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const int r = active ? wrow[rt] : 0;
+      if (LAYOUT == 0) {
+        const int64_t wr = (int64_t)e * p.N + r + (lane & 15);
+        pk[rt] = p.w_packed + wr * (K >> 2) + 16 * qa;
+        mk[rt] = p.w_mask + wr * (K >> 4) + 4 * qa;
+        sc[rt] = p.w_scale + wr * (K >> 5) + 2 * qa;
+      } else {
+        const int64_t tile = (int64_t)e * (p.N >> 4) + (r >> 4);
+        const uint8_t* rec = p.w_packed + tile * (K >> 8) * kTileRecordBytes;
+        pk[rt] = rec + 16 * lane;
+        mk[rt] = rec + kTileMaskOffset + 4 * lane;
+        sc[rt] = rec + kTileScaleOffset + 2 * lane;
+      }
+    }
+    step = LAYOUT == 0 ? 64 : kTileRecordBytes;
+  }
+
+  __device__ __forceinline__ void load(int gs, WeightFrag& w) const {
+    const int64_t op = step * gs;
+    const int64_t om = LAYOUT == 0 ? 16 * gs : op;
+    const int64_t os = LAYOUT == 0 ? 8 * gs : op;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      w.pk[rt] = *reinterpret_cast<const u32x4*>(pk[rt] + op);
+      w.mk[rt] = *reinterpret_cast<const uint32_t*>(mk[rt] + om);
+      w.sc[rt] = *reinterpret_cast<const uint16_t*>(sc[rt] + os);
+    }
+  }
+};
+
+// Compressed sparse operand of smfmac t of a fragment word, in either layout.
+template <int LAYOUT>
+__device__ __forceinline__ f16x8 weight_operand_of(uint32_t word, f16x2 s2) {
+  return LAYOUT == 0 ? weight_operand(word, s2) : weight_operand_tiled(word, s2);
+}
+
+__device__ __forceinline__ uint32_t frag_word(const u32x4& v, int t) {
+  return t == 0 ? v.x : t == 1 ? v.y : t == 2 ? v.z : v.w;
+}
+
+// Weight rows of wave `wv` in n-block `nb`: 4 row-tiles of 16. Gate/up: 32 intermediate columns,
+// i.e. gate rows c..c+31 (tiles 0, 1) and up rows I+c..I+c+31 (tiles 2, 3).
+template <int EPI>
+__device__ __forceinline__ bool wave_rows(int N, int nb, int wv, int wrow[4]) {
+  if (EPI == kEpiGateUp) {
+    const int I = N >> 1;
+    const int hcol0 = nb * 128 + wv * 32;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) wrow[rt] = (rt < 2 ? 0 : I) + hcol0 + (rt & 1) * 16;
+    return hcol0 < I;
+  } else {
+    const int r0 = nb * 256 + wv * 64;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) wrow[rt] = r0 + rt * 16;
+    return r0 < N;
+  }
+}
+
+// Expert of m-block `mb` (-1 past the last one), found by the whole workgroup in one pass.
+__device__ __forceinline__ int find_expert(const int* tile_offsets, int E, int mb, int* s_e) {
+  if (threadIdx.x == 0) *s_e = -1;
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    const int a = tile_offsets[e], b = tile_offsets[e + 1];
+    if (a <= mb && mb < b) *s_e = e;
+  }
+  __syncthreads();
+  return *s_e;
+}
+
+// Epilogues. Accumulator acc[rt][tt] of lane (n = lane & 15, q = lane >> 4) holds, for r = 0..3,
+// weight row wrow[rt] + 4q + r and the m-block's token row tt*16 + n.
+template <int EPI, int TG>
+__device__ __forceinline__ void gemm_epilogue(const GemmParams& p, f32x4 (&acc)[4][TG], int e, int row0, int m0,
+                                              int mrows, int nb, int wv, const int wrow[4], int lane) {
+  const int N = p.N, ntok = lane & 15, qa = lane >> 4;
+  const float ag = p.a_global[e];
+  if (EPI == kEpiGateUp) {
+    // h = silu(gate) * up in fp32, then the NVFP4 quantization of h with the down input global:
+    // the 32 columns of one scale group are the 8 values of each of the 4 lanes sharing ntok.
+    const int I = N >> 1;
+    const int hcol0 = nb * 128 + wv * 32;
+    const float g_gate = ag * p.w_global[2 * e];
+    const float g_up = ag * p.w_global[2 * e + 1];
+    const float g2 = p.h_global[e];
+#pragma unroll
+    for (int tt = 0; tt < TG; ++tt) {
+      if (tt * 16 >= mrows) continue;
+      const int n = tt * 16 + ntok;
+      float h[2][4];
+      float amax = 0.0f;
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float gt = acc[half][tt][r] * g_gate;
+          const float up = acc[2 + half][tt][r] * g_up;
+          const float hv = gt / (1.0f + __expf(-gt)) * up;
+          h[half][r] = hv;
+          amax = __builtin_fmaxf(amax, __builtin_fabsf(hv));
+        }
+      amax = __builtin_fmaxf(amax, __shfl_xor(amax, 16));
+      amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32));
+      const int scb = scale_code(amax, g2);
+      const float s = e4m3_value(scb);
+      if (n < mrows) {
+        const int64_t row = row0 + m0 + n;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const uint32_t c0 = nvfp4_code(h[half][0], s, g2), c1 = nvfp4_code(h[half][1], s, g2);
+          const uint32_t c2 = nvfp4_code(h[half][2], s, g2), c3 = nvfp4_code(h[half][3], s, g2);
+          const uint16_t v = (uint16_t)(c0 | (c1 << 4) | (c2 << 8) | (c3 << 12));
+          *reinterpret_cast<uint16_t*>(p.h_codes + row * (I >> 1) + ((hcol0 + half * 16 + 4 * qa) >> 1)) = v;
+        }
+        if (qa == 0) p.h_scales[row * (I >> 5) + (hcol0 >> 5)] = (uint8_t)scb;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int tt = 0; tt < TG; ++tt) {
+      if (tt * 16 >= mrows) continue;
+      const int n = tt * 16 + ntok;
+      if (n >= mrows) continue;
+      const int64_t row = row0 + m0 + n;
+      float gsc;
+      if (EPI == kEpiDown) gsc = ag * p.w_global[e] * p.topk_weights[p.sorted[row]];
+      else gsc = ag;
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const int col = wrow[rt] + 4 * qa;
+        float gcol = gsc;
+        if (EPI == kEpiStore) gcol = gsc * (p.G == 2 ? p.w_global[2 * e + (col >= (N >> 1) ? 1 : 0)] : p.w_global[e]);
+        *reinterpret_cast<f32x4*>(p.out + row * N + col) = acc[rt][tt] * gcol;
+      }
+    }
+  }
+}
+
+}  // namespace moesq

@@ -141,6 +141,35 @@ __device__ __forceinline__ f16x8 weight_operand(uint32_t kept, f16x2 s2) {
   return __builtin_bit_cast(f16x8, r);
 }
 
+// Tiled layout: the 4 kept bytes (b0 b1)(b0' b1') of one smfmac rewritten as
+// (lo b0 | lo b1 << 4, hi b0 | hi b1 << 4, lo b0' | lo b1' << 4, hi b0' | hi b1' << 4), so byte j
+// converts straight to operand slots 2j, 2j+1.
+__host__ __device__ inline uint32_t kept_to_tiled(uint32_t w) {
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+  const uint32_t x = lo | (lo >> 4);          // byte0 = lo b0 | lo b1 << 4, byte2 = lo b0' | lo b1' << 4
+  const uint32_t y = hi | (hi >> 4);          // byte0 = hi b0 | hi b1 << 4, byte2 = hi b0' | hi b1' << 4
+  return (x & 0xFFu) | ((y & 0xFFu) << 8) | (((x >> 16) & 0xFFu) << 16) | (((y >> 16) & 0xFFu) << 24);
+}
+__host__ __device__ inline uint32_t tiled_to_kept(uint32_t t) {
+  uint32_t out = 0;
+  for (int h = 0; h < 2; ++h) {                // h = 0: (b0 b1), h = 1: (b0' b1')
+    const uint32_t X = (t >> (16 * h)) & 0xFFu, Y = (t >> (16 * h + 8)) & 0xFFu;
+    const uint32_t b0 = (X & 15u) | ((Y & 15u) << 4), b1 = (X >> 4) | (Y & 0xF0u);
+    out |= (b0 | (b1 << 8)) << (16 * h);
+  }
+  return out;
+}
+
+// Compressed A operand of one smfmac from one tiled u32: 4 conversions and 4 exact products.
+__device__ __forceinline__ f16x8 weight_operand_tiled(uint32_t t, f16x2 s2) {
+  u32x4 r;
+  r.x = as_u32(fp4x2_to_f16<0>(t) * s2);
+  r.y = as_u32(fp4x2_to_f16<1>(t) * s2);
+  r.z = as_u32(fp4x2_to_f16<2>(t) * s2);
+  r.w = as_u32(fp4x2_to_f16<3>(t) * s2);
+  return __builtin_bit_cast(f16x8, r);
+}
+
 // Sparse-index word of one smfmac from the mask byte of its two chunks: each chunk's nibble q (two
 // bits set, i0 < i1) gives the 4-bit code i0 | i1 << 2 for its even group and again for its odd group.
 __host__ __device__ inline uint32_t smfmac_index_of_mask_byte(uint32_t b) {
@@ -158,5 +187,18 @@ __host__ __device__ inline uint32_t smfmac_index_of_mask_byte(uint32_t b) {
 
 // f16 value of a non-negative E4M3 scale byte (exact: E4M3 lies inside f16's range and precision).
 __device__ __forceinline__ f16 e4m3_to_f16(uint32_t b) { return (f16)e4m3_value(b); }
+
+// Both E4M3 scale bytes of a u16 (low, high) as an f16 pair: the E4M3 magnitude bits shifted into
+// an f16 field are the value times 2^-8 (normals and subnormals alike), so one packed multiply by
+// 256 gives the exact pair. The sign bits are ignored (scales are non-negative).
+__device__ __forceinline__ f16x2 scale_pair_f16(uint32_t sc16) {
+  const uint32_t bits = ((sc16 & 0x7Fu) << 7) | ((sc16 & 0x7F00u) << 15);
+  return as_f16x2(bits) * f16x2{(f16)256.0f, (f16)256.0f};
+}
+
+// Tiled weight record: 1408 bytes per (expert, 16-row tile, 256-K step).
+constexpr int kTileRecordBytes = 1408;
+constexpr int kTileMaskOffset = 1024;
+constexpr int kTileScaleOffset = 1280;
 
 }  // namespace moesq

@@ -20,6 +20,13 @@ void launch_pack(const uint8_t* dense, int64_t nbytes, uint8_t* packed, uint8_t*
                  hipStream_t stream);
 void launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t stream);
 
+// Load-time re-tiling into the kernels' weight layout (see include/moesq.h, MOESQ_LAYOUT_TILED).
+size_t tiled_bytes(int E, int N, int K);
+void launch_prepare(const uint8_t* packed, const uint8_t* mask, const uint8_t* scale, int E, int N, int K,
+                    uint8_t* tiled, hipStream_t stream);
+void launch_unprepare(const uint8_t* tiled, int E, int N, int K, uint8_t* packed, uint8_t* mask, uint8_t* scale,
+                      hipStream_t stream);
+
 // Permutation: counts[E], offsets[E+1], sorted[T*k] (live prefix), inv[T*k], tile_offsets[E+1]
 // (prefix of ceil(count/bm) for the grouped GEMM's m-blocks, when bm > 0) and status[0] (number of
 // ids outside [-1, E), which are dropped).
@@ -32,6 +39,9 @@ void launch_tile_offsets(const int* offsets, int E, int bm, int* tile_offsets, h
 enum { kEpiStore = 0, kEpiGateUp = 1, kEpiDown = 2 };
 enum { kTacticDecode = 0, kTacticPrefill = 1 };
 int tactic_rows_per_mblock(int tactic);
+// Dynamic LDS bytes of a GEMM workgroup of the tactic for reduction length K.
+size_t gemm_lds_bytes(int tactic, int K);
+constexpr size_t kMaxLdsBytes = 160 * 1024;
 
 struct GemmParams {
   // B operand: activation codes [rows][K/2], scales [rows][K/32]; expert e owns rows offsets[e]..
@@ -47,6 +57,7 @@ struct GemmParams {
   const uint8_t* w_scale;
   const float* w_global;
   int E, N, K, G;
+  int layout;                // 0 pair-bitmask storage, 1 tiled records (w_packed only)
   // kEpiStore / kEpiDown: fp32 rows [rows][N]
   float* out;
   // kEpiGateUp: h = silu(gate) * up quantized with h_global[e] into h_codes [rows][N/4], h_scales [rows][N/64]

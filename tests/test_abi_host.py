@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported():
     for name in decl:
         assert hasattr(L, name), name
     assert sorted(decl) == sorted(moesq.EXPORTED_SYMBOLS)
-    assert moesq.abi_version() == 1
+    assert moesq.abi_version() == 2
 
 
 def test_status_strings():
@@ -92,6 +92,28 @@ def test_argument_checks_return_status_without_launching():
     assert L.moesq_validate_weights(P, 4, 40, P, None) == INVALID
     assert L.moesq_unpack_pair_bitmask(P, P, 4, 40, P, P, None) == INVALID
     assert L.moesq_pack_pair_bitmask(P, 4, 40, P, P, P, None) == INVALID
+
+
+def test_tiled_layout_size_and_checks():
+    L = moesq.lib()
+    assert L.moesq_tiled_bytes(128, 1536, 2048) == 128 * (1536 // 16) * (2048 // 256) * 1408
+    assert L.moesq_tiled_bytes(128, 1536, 2048) == 128 * 1536 * 2048 * 11 // 32     # same bytes as stored
+    assert L.moesq_tiled_bytes(1, 24, 256) == 0 and L.moesq_tiled_bytes(1, 16, 96) == 0
+    P = ctypes.c_void_p(16)
+    w = _weights(E=2, N=64, K=256)
+    w.layout = 1
+    assert L.moesq_prepare_weights(ctypes.byref(w), P, None) == INVALID        # source must be pair-bitmask
+    w.layout = 0
+    w.N = 24
+    assert L.moesq_prepare_weights(ctypes.byref(w), P, None) == UNSUPPORTED
+    bad = _weights()
+    bad.layout = 7
+    assert L.moesq_grouped_gemm(P, P, P, P, 4, ctypes.byref(bad), P, P, 1 << 20, None) == INVALID
+    tiled = _weights()
+    tiled.layout = 1
+    tiled.mask = None
+    tiled.scale = None
+    assert L.moesq_grouped_gemm(P, P, P, P, 4, ctypes.byref(tiled), P, P, 4, None) == WORKSPACE  # past the layout checks
 
 
 def test_binding_refuses_cpu_tensors():

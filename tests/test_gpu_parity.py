@@ -179,16 +179,56 @@ def test_storage_codec_bit_exact():
     assert moesq.validate_weights(torch.from_numpy(mbad).to(DEV), K) == pairbitmask.invalid_nibbles(mbad) == 3
 
 
+def _tiled_reference(packed, mask, scale):
+    """The tiled record bytes, written out from the layout's definition in include/moesq.h."""
+    E, N, Kq = packed.shape
+    K = Kq * 4
+    steps = K // 256
+    out = np.zeros((E, N // 16, steps, 1408), np.uint8)
+    lo, hi = packed & 0x0F, packed >> 4
+    for e in range(E):
+        for tile in range(N // 16):
+            for ss in range(steps):
+                for lane in range(64):
+                    row, q = tile * 16 + lane % 16, lane // 16
+                    kb = (ss * 256 + 64 * q) // 4                    # packed byte offset of the lane's 64 K
+                    for t in range(4):                               # smfmac t: bytes (b0 b1)(b0' b1')
+                        b = kb + 4 * t
+                        rec = out[e, tile, ss]
+                        rec[16 * lane + 4 * t + 0] = lo[e, row, b] | (lo[e, row, b + 1] << 4)
+                        rec[16 * lane + 4 * t + 1] = hi[e, row, b] | (hi[e, row, b + 1] << 4)
+                        rec[16 * lane + 4 * t + 2] = lo[e, row, b + 2] | (lo[e, row, b + 3] << 4)
+                        rec[16 * lane + 4 * t + 3] = hi[e, row, b + 2] | (hi[e, row, b + 3] << 4)
+                    m0 = (ss * 256 + 64 * q) // 16
+                    out[e, tile, ss, 1024 + 4 * lane: 1028 + 4 * lane] = mask[e, row, m0:m0 + 4]
+                    s0 = (ss * 256 + 64 * q) // 32
+                    out[e, tile, ss, 1280 + 2 * lane: 1282 + 2 * lane] = scale[e, row, s0:s0 + 2]
+    return out.reshape(-1)
+
+
+def test_prepare_layout_and_round_trip():
+    E, N, K = 2, 32, 512
+    packed, mask, scale, gw = synth.random_sparse_weights(30, E, N, K, 1)
+    w = moesq.SparseWeights(*(torch.from_numpy(np.ascontiguousarray(t)).to(DEV) for t in (packed, mask, scale, gw)))
+    wt = moesq.prepare_weights(w)
+    assert np.array_equal(wt.packed.cpu().numpy(), _tiled_reference(packed, mask, scale))
+    back = moesq.unprepare_weights(wt)
+    for a, b in ((back.packed, packed), (back.mask, mask), (back.scale, scale)):
+        assert np.array_equal(a.cpu().numpy(), b)
+
+
 # ------------------------------------------------------------------------------------------------
 # grouped GEMM
 # ------------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("layout", [0, 1])
 @pytest.mark.parametrize("E,N,K,G,counts", [
     (1, 256, 512, 1, [16]),                                       # one expert linear
     (4, 256, 512, 2, [0, 5, 33, 17]),                             # ragged, an empty expert, decode tactic
     (3, 320, 768, 1, [200, 0, 130]),                              # prefill tactic, N not a multiple of 256
     (2, 64, 2048, 2, [1, 129]),
+    (5, 128, 1280, 1, [40, 3, 0, 31, 64]),                        # decode, K-chunks of 512 with a short last one
 ])
-def test_grouped_gemm_random_bytes(E, N, K, G, counts):
+def test_grouped_gemm_random_bytes(E, N, K, G, counts, layout):
     packed, mask, scale, gw = synth.random_sparse_weights(12, E, N, K, G)
     scale = np.clip(scale, 0x18, 0x60).astype(np.uint8)            # keep products in a sane exponent range
     rows = sum(counts)
@@ -197,6 +237,8 @@ def test_grouped_gemm_random_bytes(E, N, K, G, counts):
     a_global = (2.0 ** np.random.default_rng(1).uniform(-6, -2, E)).astype(np.float32)
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     w = moesq.SparseWeights(*(torch.from_numpy(np.ascontiguousarray(t)).to(DEV) for t in (packed, mask, scale, gw)))
+    if layout == 1:
+        w = moesq.prepare_weights(w)
     out = moesq.grouped_gemm(torch.from_numpy(a_codes).to(DEV), torch.from_numpy(a_scales).to(DEV),
                              torch.from_numpy(a_global).to(DEV), torch.from_numpy(offsets).to(DEV), w)
     ref = moe.grouped_gemm(a_codes, a_scales, a_global, offsets, packed, mask, scale, gw)
@@ -227,10 +269,12 @@ def test_linear_workload():
 # ------------------------------------------------------------------------------------------------
 # MoE FFN
 # ------------------------------------------------------------------------------------------------
-def _layer(seed, E, H, I):
+def _layer(seed, E, H, I, tiled=True):
     def dense_expert(e):       # regenerated on demand (deterministic), not cached
         return synth.expert_dense_weights(seed, e, H, I, device=DEV)
     w13, w2 = moesq.compress_moe_layer(E, H, I, dense_expert, device=DEV)
+    if tiled:
+        w13, w2 = moesq.prepare_weights(w13), moesq.prepare_weights(w2)
     return w13, w2, dense_expert
 
 
@@ -259,12 +303,14 @@ def _run_ffn(x, ids, wts, w13, w2, g13, g2):
     return out.cpu().numpy(), inter
 
 
-@pytest.mark.parametrize("E,H,I,T,k,fixed", [(8, 512, 256, 64, 4, False),     # decode tactic
-                                              (8, 512, 256, 512, 4, False),    # prefill tactic
-                                              (6, 256, 512, 40, 3, True)])     # saturating 1/2688 globals
-def test_moe_ffn_small(E, H, I, T, k, fixed):
+@pytest.mark.parametrize("E,H,I,T,k,fixed,tiled", [(8, 512, 256, 64, 4, False, True),     # decode tactic
+                                                    (8, 512, 256, 64, 4, False, False),    # stored layout
+                                                    (8, 512, 256, 512, 4, False, True),    # prefill tactic
+                                                    (8, 512, 256, 512, 4, False, False),
+                                                    (6, 256, 512, 40, 3, True, True)])     # 1/2688 globals
+def test_moe_ffn_small(E, H, I, T, k, fixed, tiled):
     from ffn_check import compare_ffn, oracle_layer
-    w13, w2, dense_expert = _layer(21, E, H, I)
+    w13, w2, dense_expert = _layer(21, E, H, I, tiled)
     x = synth.activations(22, T, H, device=DEV)
     ids, wts = synth.routing(23, T, E, k)
     g13, g2 = _globals(x, ids, E, dense_expert, fixed)
