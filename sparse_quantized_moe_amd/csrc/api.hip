@@ -2,7 +2,7 @@
 #include <string>
 #include <cstdio>
 
-#include "../../include/moesq.h"
+#include "moesq.h"
 #include "moesq_internal.h"
 
 namespace {

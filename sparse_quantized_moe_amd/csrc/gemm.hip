@@ -44,118 +44,119 @@ __host__ __device__ constexpr int dec_kc(int TG) { return kDecLdsB / (TG * 16 * 
 // lane's two chunks are one contiguous 32-byte read.
 __device__ __forceinline__ int dec_chunk_pos(int c) { return ((c & 15) << 1) | (c >> 4); }
 
-template <int EPI, int LAYOUT, int TG>
-__global__ __launch_bounds__(kGemmThreads) void k_gemm_decode(GemmParams p) {
-  constexpr int BMT = TG * 16;
+// One workgroup per (expert, n-block): the expert comes straight from the block index, so the only
+// round trip before the weight stream starts is the read of the expert's row range; experts with
+// more than 32 rows are covered by further passes over the same (now cache-resident) weights.
+template <int EPI, int LAYOUT, int RT>
+__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(3))) void k_gemm_decode(GemmParams p) {
+  constexpr int TG = 2, BMT = TG * 16;
   constexpr int KCMAX = dec_kc(TG);
   constexpr int RS = KCMAX * 2 + 16;                              // LDS bytes per token row (+16 B skew)
   extern __shared__ __align__(16) uint8_t smem[];
-  __shared__ int s_e;
   const int K = p.K;
   uint8_t* sB = smem;                                             // [BMT][RS] f16, chunk pairs adjacent
   uint16_t* lut_idx = reinterpret_cast<uint16_t*>(smem + BMT * RS);   // [256]
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int mb = blockIdx.x, nb = blockIdx.y;
-  lut_idx[tid] = (uint16_t)smfmac_index_of_mask_byte((uint32_t)tid);
-  const int e = find_expert(p.tile_offsets, p.E, mb, &s_e);
-  if (e < 0) return;
+  const int e = blockIdx.x, nb = blockIdx.y;
   const int row0 = p.offsets[e];
   const int M = p.offsets[e + 1] - row0;
-  const int m0 = (mb - p.tile_offsets[e]) * BMT;
-  const int mrows = M - m0 < BMT ? M - m0 : BMT;
-  const int ntiles = (mrows + 15) >> 4;
+  if (M <= 0) return;
+  lut_idx[tid] = (uint16_t)smfmac_index_of_mask_byte((uint32_t)tid);
 
-  int wrow[4];
-  const bool active = wave_rows<EPI>(p.N, nb, wv, wrow);
-  WeightPtrs<LAYOUT> wp;
+  int wrow[RT];
+  const bool active = wave_rows<EPI, RT>(p.N, nb, wv, wrow);
+  WeightPtrs<LAYOUT, RT> wp;
   wp.init(p, e, wrow, active, lane);
   const int nsteps = K >> 8;
   constexpr int spc = KCMAX >> 8;                                 // super-steps per staged chunk
-  WeightFrag w0, w1, w2;
-  if (active) {
-    wp.load(0, w0);
-    if (nsteps > 1) wp.load(1, w1);
-  }
-  f32x4 acc[4][TG];
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-    for (int tt = 0; tt < TG; ++tt) acc[rt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
   const int nrow = lane & 15, qb = lane >> 4;
-  const int64_t arow = (int64_t)(row0 + m0) * (K >> 1);
-  const int64_t srow = (int64_t)(row0 + m0) * (K >> 5);
-  auto step = [&](int gs, const WeightFrag& w) {
-    const int ssl = gs % spc;
-    if (ssl == 0) {
-      // stage the K-chunk [k0, k0 + kc) of the m-block's activations as exact f16
-      const int k0 = gs * 256;
-      const int kc = K - k0 < KCMAX ? K - k0 : KCMAX;
-      const int quads = kc >> 5;                                  // 4-chunk groups (32 K) per row
-      __syncthreads();
-      for (int i = tid; i < ntiles * 16 * quads; i += kGemmThreads) {
-        const int n = i / quads, q4 = i - n * quads;
-        u32x4 v = u32x4{0u, 0u, 0u, 0u};
-        uint32_t sb = 0;
-        if (n < mrows) {
-          v = *reinterpret_cast<const u32x4*>(p.a_codes + arow + (int64_t)n * (K >> 1) + (k0 >> 1) + q4 * 16);
-          sb = p.a_scales[srow + (int64_t)n * (K >> 5) + (k0 >> 5) + q4];
-        }
-        const f16 s = e4m3_to_f16(sb);
-        const f16x2 s2 = f16x2{s, s};
-        const uint32_t wv4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int c = 4 * q4 + j;                               // chunk within the staged K-chunk
-          const int pos = (c & ~31) + dec_chunk_pos(c & 31);
-          *reinterpret_cast<u32x4*>(sB + n * RS + pos * 16) = act_chunk_kprime(wv4[j], s2);
-        }
-      }
-      __syncthreads();
+
+  for (int m0 = 0; m0 < M; m0 += BMT) {
+    const int mrows = M - m0 < BMT ? M - m0 : BMT;
+    const int ntiles = (mrows + 15) >> 4;
+    WeightFrag<RT> w0, w1, w2;
+    if (active) {
+      wp.load(0, w0);
+      if (nsteps > 1) wp.load(1, w1);
     }
-    if (!active) return;
+    f32x4 acc[RT][TG];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      f16x8 A[4];
-      int idx[4];
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        const f16x2 sp = scale_pair_f16(w.sc[rt]);
-        const f16x2 s2 = (t < 2) ? __builtin_shufflevector(sp, sp, 0, 0) : __builtin_shufflevector(sp, sp, 1, 1);
-        A[rt] = weight_operand_of<LAYOUT>(frag_word(w.pk[rt], t), s2);
-        idx[rt] = lut_idx[(w.mk[rt] >> (8 * t)) & 255u];
+      for (int tt = 0; tt < TG; ++tt) acc[rt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int64_t arow = (int64_t)(row0 + m0) * (K >> 1);
+    const int64_t srow = (int64_t)(row0 + m0) * (K >> 5);
+    auto step = [&](int gs, const WeightFrag<RT>& w) {
+      const int ssl = gs % spc;
+      if (ssl == 0) {
+        // stage the K-chunk [k0, k0 + kc) of the m-block's activations as exact f16
+        const int k0 = gs * 256;
+        const int kc = K - k0 < KCMAX ? K - k0 : KCMAX;
+        const int quads = kc >> 5;                                // 4-chunk groups (32 K) per row
+        __syncthreads();
+        for (int i = tid; i < ntiles * 16 * quads; i += kGemmThreads) {
+          const int n = i / quads, q4 = i - n * quads;
+          u32x4 v = u32x4{0u, 0u, 0u, 0u};
+          uint32_t sb = 0;
+          if (n < mrows) {
+            v = *reinterpret_cast<const u32x4*>(p.a_codes + arow + (int64_t)n * (K >> 1) + (k0 >> 1) + q4 * 16);
+            sb = p.a_scales[srow + (int64_t)n * (K >> 5) + (k0 >> 5) + q4];
+          }
+          const f16 s = e4m3_to_f16(sb);
+          const f16x2 s2 = f16x2{s, s};
+          const uint32_t wv4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int c = 4 * q4 + j;                             // chunk within the staged K-chunk
+            const int pos = (c & ~31) + dec_chunk_pos(c & 31);
+            *reinterpret_cast<u32x4*>(sB + n * RS + pos * 16) = act_chunk_kprime(wv4[j], s2);
+          }
+        }
+        __syncthreads();
       }
-      const int c0 = 8 * (qb >> 1) + 2 * t + (qb & 1);
+      if (!active) return;
 #pragma unroll
-      for (int tt = 0; tt < TG; ++tt) {
-        if (tt < ntiles) {
-          const uint8_t* bp = sB + (tt * 16 + nrow) * RS + (32 * ssl + 2 * c0) * 16;
-          const u32x4 b0 = *reinterpret_cast<const u32x4*>(bp);
-          const u32x4 b1 = *reinterpret_cast<const u32x4*>(bp + 16);
-          const f16x16 B = __builtin_bit_cast(f16x16, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
+      for (int t = 0; t < 4; ++t) {
+        f16x8 A[RT];
+        int idx[RT];
 #pragma unroll
-          for (int rt = 0; rt < 4; ++rt)
-            acc[rt][tt] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(A[rt], B, acc[rt][tt], idx[rt], 0, 0);
+        for (int rt = 0; rt < RT; ++rt) {
+          const f16x2 sp = scale_pair_f16(w.sc[rt]);
+          const f16x2 s2 = (t < 2) ? __builtin_shufflevector(sp, sp, 0, 0) : __builtin_shufflevector(sp, sp, 1, 1);
+          A[rt] = weight_operand_of<LAYOUT>(frag_word(w.pk[rt], t), s2);
+          idx[rt] = lut_idx[(w.mk[rt] >> (8 * t)) & 255u];
+        }
+        const int c0 = 8 * (qb >> 1) + 2 * t + (qb & 1);
+#pragma unroll
+        for (int tt = 0; tt < TG; ++tt) {
+          if (tt < ntiles) {
+            const uint8_t* bp = sB + (tt * 16 + nrow) * RS + (32 * ssl + 2 * c0) * 16;
+            const u32x4 b0 = *reinterpret_cast<const u32x4*>(bp);
+            const u32x4 b1 = *reinterpret_cast<const u32x4*>(bp + 16);
+            const f16x16 B = __builtin_bit_cast(f16x16, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+              acc[rt][tt] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(A[rt], B, acc[rt][tt], idx[rt], 0, 0);
+          }
         }
       }
+    };
+    // Three-slot register ring, unrolled by its period so no register of a load in flight is ever
+    // copied: step gs reads slot gs % 3 while the loads of gs + 1 and gs + 2 are outstanding.
+    int gs = 0;
+    for (; gs + 3 <= nsteps; gs += 3) {
+      if (active && gs + 2 < nsteps) wp.load(gs + 2, w2);
+      step(gs, w0);
+      if (active && gs + 3 < nsteps) wp.load(gs + 3, w0);
+      step(gs + 1, w1);
+      if (active && gs + 4 < nsteps) wp.load(gs + 4, w1);
+      step(gs + 2, w2);
     }
-  };
-  // Three-slot register ring, unrolled by its period so no register of a load in flight is ever
-  // copied: step gs reads slot gs % 3 while the loads of gs + 1 and gs + 2 are outstanding.
-  int gs = 0;
-  for (; gs + 3 <= nsteps; gs += 3) {
-    if (active && gs + 2 < nsteps) wp.load(gs + 2, w2);
-    step(gs, w0);
-    if (active && gs + 3 < nsteps) wp.load(gs + 3, w0);
-    step(gs + 1, w1);
-    if (active && gs + 4 < nsteps) wp.load(gs + 4, w1);
-    step(gs + 2, w2);
+    if (gs < nsteps) step(gs, w0);
+    if (gs + 1 < nsteps) step(gs + 1, w1);
+    if (active) gemm_epilogue<EPI, TG, RT>(p, acc, e, row0, m0, mrows, nb, wv, wrow, lane);
   }
-  if (gs < nsteps) step(gs, w0);
-  if (gs + 1 < nsteps) step(gs + 1, w1);
-  if (!active) return;
-  gemm_epilogue<EPI, TG>(p, acc, e, row0, m0, mrows, nb, wv, wrow, lane);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -196,12 +197,12 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_prefill(GemmParams p) {
     for (int tt = 0; tt < kPreTG; ++tt) acc[rt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nsteps = K >> 8;
-  WeightFrag wa, wb;
+  WeightFrag<> wa, wb;
   if (active) wp.load(0, wa);
   const int64_t a_row_bytes = K >> 1, a_row_scales = K >> 5;
   // one 256-K step: stage the activations of this K range into LDS, prefetch the next weight
   // fragment into `nxt`, run the MFMAs on `cur`
-  auto step = [&](int gs, const WeightFrag& cur, WeightFrag& nxt) {
+  auto step = [&](int gs, const WeightFrag<>& cur, WeightFrag<>& nxt) {
     const int k0 = gs * 256;
     __syncthreads();
     for (int i = tid; i < kPreBMT * 32; i += kGemmThreads) {
@@ -277,11 +278,13 @@ static void set_lds_attr(Kern* k, size_t lds) {
 
 template <int EPI, int LAYOUT>
 static void launch_decode(const GemmParams& p, hipStream_t stream) {
+  // gate/up waves own 4 row-tiles (32 columns for the fused quantization); other linears stream
+  // 2 row-tiles per wave, which keeps more, shorter streams in flight for short K
+  constexpr int RT = EPI == kEpiGateUp ? 4 : 2;
   const size_t lds = gemm_lds_bytes(kTacticDecode, p.K);
-  set_lds_attr(&k_gemm_decode<EPI, LAYOUT, kDecTG>, lds);
-  const int64_t mblocks = (p.rows + kDecTG * 16 - 1) / (kDecTG * 16) + p.E;
-  const int nblocks = EPI == kEpiGateUp ? ((p.N >> 1) + 127) / 128 : (p.N + 255) / 256;
-  k_gemm_decode<EPI, LAYOUT, kDecTG><<<dim3((unsigned)mblocks, (unsigned)nblocks), kGemmThreads, lds, stream>>>(p);
+  set_lds_attr(&k_gemm_decode<EPI, LAYOUT, RT>, lds);
+  const int nblocks = EPI == kEpiGateUp ? ((p.N >> 1) + 127) / 128 : (p.N + 64 * RT - 1) / (64 * RT);
+  k_gemm_decode<EPI, LAYOUT, RT><<<dim3((unsigned)p.E, (unsigned)nblocks), kGemmThreads, lds, stream>>>(p);
 }
 
 template <int EPI, int LAYOUT>

@@ -8,51 +8,69 @@ namespace moesq {
 
 // Kept bytes, masks and scales one lane needs for one 256-K super-step of 4 row-tiles: 16 B of
 // packed, 4 B of mask and 2 B of scale per row-tile (the lane's 64 contiguous K of its row).
+template <int RT = 4>
 struct WeightFrag {
-  u32x4 pk[4];
-  uint32_t mk[4];
-  uint32_t sc[4];
+  u32x4 pk[RT];
+  uint32_t mk[RT];
+  uint32_t sc[RT];
 };
 
 // LAYOUT 0: pair-bitmask storage (three row-major tensors); LAYOUT 1: tiled records, one
 // contiguous 1408-byte record per (16-row tile, 256-K step), so each load of a wave is coalesced.
-template <int LAYOUT>
-struct WeightPtrs {
-  const uint8_t* pk[4];
-  const uint8_t* mk[4];
-  const uint8_t* sc[4];
-  int64_t step;   // bytes between consecutive 256-K steps of the packed pointer
+template <int LAYOUT, int RT = 4>
+struct WeightPtrs;
 
-  __device__ __forceinline__ void init(const GemmParams& p, int e, const int wrow[4], bool active, int lane) {
+template <int RT>
+struct WeightPtrs<0, RT> {
+  const uint8_t* pk[RT];
+  const uint8_t* mk[RT];
+  const uint8_t* sc[RT];
+
+  __device__ __forceinline__ void init(const GemmParams& p, int e, const int* wrow, bool active, int lane) {
     const int K = p.K, qa = lane >> 4;
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      const int r = active ? wrow[rt] : 0;
-      if (LAYOUT == 0) {
-        const int64_t wr = (int64_t)e * p.N + r + (lane & 15);
-        pk[rt] = p.w_packed + wr * (K >> 2) + 16 * qa;
-        mk[rt] = p.w_mask + wr * (K >> 4) + 4 * qa;
-        sc[rt] = p.w_scale + wr * (K >> 5) + 2 * qa;
-      } else {
-        const int64_t tile = (int64_t)e * (p.N >> 4) + (r >> 4);
-        const uint8_t* rec = p.w_packed + tile * (K >> 8) * kTileRecordBytes;
-        pk[rt] = rec + 16 * lane;
-        mk[rt] = rec + kTileMaskOffset + 4 * lane;
-        sc[rt] = rec + kTileScaleOffset + 2 * lane;
-      }
+    for (int rt = 0; rt < RT; ++rt) {
+      const int64_t wr = (int64_t)e * p.N + (active ? wrow[rt] : 0) + (lane & 15);
+      pk[rt] = p.w_packed + wr * (K >> 2) + 16 * qa;
+      mk[rt] = p.w_mask + wr * (K >> 4) + 4 * qa;
+      sc[rt] = p.w_scale + wr * (K >> 5) + 2 * qa;
     }
-    step = LAYOUT == 0 ? 64 : kTileRecordBytes;
   }
 
-  __device__ __forceinline__ void load(int gs, WeightFrag& w) const {
-    const int64_t op = step * gs;
-    const int64_t om = LAYOUT == 0 ? 16 * gs : op;
-    const int64_t os = LAYOUT == 0 ? 8 * gs : op;
+  __device__ __forceinline__ void load(int gs, WeightFrag<RT>& w) const {
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      w.pk[rt] = *reinterpret_cast<const u32x4*>(pk[rt] + op);
-      w.mk[rt] = *reinterpret_cast<const uint32_t*>(mk[rt] + om);
-      w.sc[rt] = *reinterpret_cast<const uint16_t*>(sc[rt] + os);
+    for (int rt = 0; rt < RT; ++rt) {
+      w.pk[rt] = *reinterpret_cast<const u32x4*>(pk[rt] + 64 * gs);
+      w.mk[rt] = *reinterpret_cast<const uint32_t*>(mk[rt] + 16 * gs);
+      w.sc[rt] = *reinterpret_cast<const uint16_t*>(sc[rt] + 8 * gs);
+    }
+  }
+};
+
+template <int RT>
+struct WeightPtrs<1, RT> {
+  const uint8_t* base[RT];  // wave-uniform record pointer of each row-tile's first step
+  int lane16;               // lane offsets inside a record
+
+  __device__ __forceinline__ void init(const GemmParams& p, int e, const int* wrow, bool active, int lane) {
+    const int steps = p.K >> 8;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int r = __builtin_amdgcn_readfirstlane(active ? wrow[rt] : 0);
+      const int64_t tile = (int64_t)e * (p.N >> 4) + (r >> 4);
+      base[rt] = p.w_packed + tile * steps * kTileRecordBytes;
+    }
+    lane16 = lane;
+  }
+
+  __device__ __forceinline__ void load(int gs, WeightFrag<RT>& w) const {
+    const int64_t off = (int64_t)gs * kTileRecordBytes;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const uint8_t* rec = base[rt] + off;
+      w.pk[rt] = *reinterpret_cast<const u32x4*>(rec + 16 * lane16);
+      w.mk[rt] = *reinterpret_cast<const uint32_t*>(rec + kTileMaskOffset + 4 * lane16);
+      w.sc[rt] = *reinterpret_cast<const uint16_t*>(rec + kTileScaleOffset + 2 * lane16);
     }
   }
 };
@@ -67,20 +85,23 @@ __device__ __forceinline__ uint32_t frag_word(const u32x4& v, int t) {
   return t == 0 ? v.x : t == 1 ? v.y : t == 2 ? v.z : v.w;
 }
 
-// Weight rows of wave `wv` in n-block `nb`: 4 row-tiles of 16. Gate/up: 32 intermediate columns,
-// i.e. gate rows c..c+31 (tiles 0, 1) and up rows I+c..I+c+31 (tiles 2, 3).
-template <int EPI>
-__device__ __forceinline__ bool wave_rows(int N, int nb, int wv, int wrow[4]) {
-  if (EPI == kEpiGateUp) {
+// Weight rows of wave `wv` in n-block `nb`: RT row-tiles of 16 (n-blocks of 4 * 16 * RT rows).
+// Gate/up (RT = 4): 32 intermediate columns, i.e. gate rows c..c+31 (tiles 0, 1) and up rows
+// I+c..I+c+31 (tiles 2, 3), n-blocks of 128 columns.
+template <int EPI, int RT = 4>
+__device__ __forceinline__ bool wave_rows(int N, int nb, int wv_in, int* wrow) {
+  const int wv = __builtin_amdgcn_readfirstlane(wv_in);
+  if constexpr (EPI == kEpiGateUp) {
+    static_assert(EPI != kEpiGateUp || RT == 4, "gate/up waves own 2 gate and 2 up tiles");
     const int I = N >> 1;
     const int hcol0 = nb * 128 + wv * 32;
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) wrow[rt] = (rt < 2 ? 0 : I) + hcol0 + (rt & 1) * 16;
+    for (int rt = 0; rt < RT; ++rt) wrow[rt] = (rt < 2 ? 0 : I) + hcol0 + (rt & 1) * 16;
     return hcol0 < I;
   } else {
-    const int r0 = nb * 256 + wv * 64;
+    const int r0 = (nb * 4 + wv) * 16 * RT;
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) wrow[rt] = r0 + rt * 16;
+    for (int rt = 0; rt < RT; ++rt) wrow[rt] = r0 + rt * 16;
     return r0 < N;
   }
 }
@@ -99,16 +120,16 @@ __device__ __forceinline__ int find_expert(const int* tile_offsets, int E, int m
 
 // Epilogues. Accumulator acc[rt][tt] of lane (n = lane & 15, q = lane >> 4) holds, for r = 0..3,
 // weight row wrow[rt] + 4q + r and the m-block's token row tt*16 + n.
-template <int EPI, int TG>
-__device__ __forceinline__ void gemm_epilogue(const GemmParams& p, f32x4 (&acc)[4][TG], int e, int row0, int m0,
-                                              int mrows, int nb, int wv, const int wrow[4], int lane) {
+template <int EPI, int TG, int RT = 4>
+__device__ __forceinline__ void gemm_epilogue(const GemmParams& p, f32x4 (&acc)[RT][TG], int e, int row0, int m0,
+                                              int mrows, int nb, int wv, const int* wrow, int lane) {
   const int N = p.N, ntok = lane & 15, qa = lane >> 4;
   const float ag = p.a_global[e];
-  if (EPI == kEpiGateUp) {
+  if constexpr (EPI == kEpiGateUp) {
     // h = silu(gate) * up in fp32, then the NVFP4 quantization of h with the down input global:
     // the 32 columns of one scale group are the 8 values of each of the 4 lanes sharing ntok.
     const int I = N >> 1;
-    const int hcol0 = nb * 128 + wv * 32;
+    const int hcol0 = nb * 128 + __builtin_amdgcn_readfirstlane(wv) * 32;
     const float g_gate = ag * p.w_global[2 * e];
     const float g_up = ag * p.w_global[2 * e + 1];
     const float g2 = p.h_global[e];
@@ -155,7 +176,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, f32x4 (&acc)[
       if (EPI == kEpiDown) gsc = ag * p.w_global[e] * p.topk_weights[p.sorted[row]];
       else gsc = ag;
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
+      for (int rt = 0; rt < RT; ++rt) {
         const int col = wrow[rt] + 4 * qa;
         float gcol = gsc;
         if (EPI == kEpiStore) gcol = gsc * (p.G == 2 ? p.w_global[2 * e + (col >= (N >> 1) ? 1 : 0)] : p.w_global[e]);
