@@ -53,6 +53,11 @@ class HipEvents:
                 raise RuntimeError("hipEventCreate failed")
         return arr
 
+    def record(self, e) -> None:
+        import torch
+        if self.hip.hipEventRecord(ctypes.c_void_p(e), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
     def elapsed_ms(self, a, b) -> float:
         ms = ctypes.c_float()
         if self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
@@ -106,29 +111,39 @@ def touched_bytes(ids, E, H, I):
     return n, n * per
 
 
-def run_steps(moesq, torch, ev, x, ids_t, wts_t, layers, g13_t, g2_t, out, ws, warmup, steps):
+def run_steps(moesq, torch, ev, x, ids_t, wts_t, layers, g13_t, g2_t, out, ws, warmup, steps, staged=False):
     """Untimed warmup, then exactly ``steps`` timed calls bracketed by synchronizations.
-    Returns (wall seconds, per-step stage times [steps][5] in ms)."""
+
+    Returns (wall seconds, stage times [steps][stages] in ms or None, GPU ms per step). Without
+    ``staged`` the calls run back to back with HIP events only around the whole region; with it every
+    call records events between its stages (on the library's stream), which adds a little time."""
     nl = len(layers)
+    ns = len(moesq.FFN_STAGES)
     for i in range(warmup):
         w13, w2 = layers[i % nl]
         moesq.moe_ffn(x, ids_t, wts_t, w13, w2, g13_t, g2_t, out=out, workspace=ws)
     torch.cuda.synchronize()
-    evs = [ev.create(6) for _ in range(steps)]
+    evs = [ev.create(ns + 1) for _ in range(steps)] if staged else []
+    region = ev.create(2)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev.record(region[0])
     for i in range(steps):
         w13, w2 = layers[i % nl]
-        moesq.set_stage_events(evs[i])
+        if staged:
+            moesq.set_stage_events(evs[i])
         moesq.moe_ffn(x, ids_t, wts_t, w13, w2, g13_t, g2_t, out=out, workspace=ws)
+    ev.record(region[1])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    moesq.set_stage_events(None)
-    stages = np.array([[ev.elapsed_ms(e[j], e[j + 1]) for j in range(5)] for e in evs])
-    total = np.array([ev.elapsed_ms(e[0], e[5]) for e in evs])
-    for e in evs:
+    gpu_ms = ev.elapsed_ms(region[0], region[1]) / steps
+    stages = None
+    if staged:
+        moesq.set_stage_events(None)
+        stages = np.array([[ev.elapsed_ms(e[j], e[j + 1]) for j in range(ns)] for e in evs])
+    for e in evs + [region]:
         ev.destroy(e)
-    return wall, stages, total
+    return wall, stages, gpu_ms
 
 
 def cpu_baseline(wl, seed, x, ids, wts, g13, g2, dense_expert, ntok):
@@ -207,24 +222,28 @@ def main():
                      device=dev)
     out = torch.empty((wl.T, wl.H), dtype=torch.float32, device=dev)
 
-    wall, stages, total = run_steps(moesq, torch, ev, x, ids_t, wts_t, layers, g13_t, g2_t, out, ws,
-                                    args.warmup, args.steps)
+    wall, _, gpu_ms = run_steps(moesq, torch, ev, x, ids_t, wts_t, layers, g13_t, g2_t, out, ws,
+                                args.warmup, args.steps)
     ms = wall / args.steps * 1e3
     n_touched, wbytes = touched_bytes(ids, wl.E, wl.H, wl.I)
     value = wbytes / (wall / args.steps) / 1e9
+    log(f"decode: {ms * 1e3:.1f} us/step wall, {gpu_ms * 1e3:.1f} us/step GPU events, {value:.1f} GB/s")
+    # stage breakdown (events between the stages of every call), same rotation of weight copies
+    _, stages, st_gpu = run_steps(moesq, torch, ev, x, ids_t, wts_t, layers, g13_t, g2_t, out, ws,
+                                  args.warmup, args.steps, staged=True)
     st_mean = stages.mean(axis=0)
-    log("decode stage ms (mean): " + ", ".join(f"{n}={v * 1e3:.1f}us" for n, v in zip(moesq.FFN_STAGES, st_mean)))
-    log(f"decode: {ms * 1e3:.1f} us/step wall, {total.mean() * 1e3:.1f} us/step events, {value:.1f} GB/s")
+    log("decode stage us (mean): " + ", ".join(f"{n}={v * 1e3:.1f}" for n, v in zip(moesq.FFN_STAGES, st_mean))
+        + f"; {st_gpu * 1e3:.1f} us/step with stage events")
     # warm (single copy) figure
-    wall_w, _, total_w = run_steps(moesq, torch, ev, x, ids_t, wts_t, layers[:1], g13_t, g2_t, out, ws,
-                                   args.warmup, args.steps)
+    wall_w, _, _ = run_steps(moesq, torch, ev, x, ids_t, wts_t, layers[:1], g13_t, g2_t, out, ws,
+                             args.warmup, args.steps)
     warm = wbytes / (wall_w / args.steps) / 1e9
     # dominant kernel: gate/up GEMM; algorithmic bytes = W13 stored bytes of touched experts + its
     # activation input (codes + scales) + its output (down-input codes + scales)
     P = int((ids >= 0).sum())
     w13_bytes = n_touched * (2 * wl.I * wl.H * 11 // 32 + 8)
     gemm_bytes = w13_bytes + P * (wl.H // 2 + wl.H // 32) + P * (wl.I // 2 + wl.I // 32)
-    gemm_ms = float(st_mean[2])
+    gemm_ms = float(st_mean[moesq.FFN_STAGES.index("gemm_gate_up")])
     achieved = gemm_bytes / (gemm_ms * 1e-3) / 1e9
     traffic = None
     tfile = os.path.join(ROOT, "profiles", "traffic_gemm_gate_up_qwen3_30b_decode.json")
@@ -240,6 +259,7 @@ def main():
         "config": {"workload": wl.name, "experts": wl.E, "top_k": wl.k, "hidden": wl.H, "moe_intermediate": wl.I,
                    "tokens": wl.T, "experts_touched": n_touched, "stored_bytes_streamed": wbytes,
                    "weight_copies_rotated": args.copies, "warm_cache_GBps": round(warm, 2),
+                   "gpu_us_per_step": round(gpu_ms * 1e3, 2),
                    "stage_us": {n: round(float(v) * 1e3, 2) for n, v in zip(moesq.FFN_STAGES, st_mean)}},
         "roofline": {"bound": "hbm", "kernel": "k_grouped_gemm<gate_up> (decode tactic)", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -258,13 +278,14 @@ def main():
                           dtype=torch.uint8, device=dev)
         pout = torch.empty((pw.T, pw.H), dtype=torch.float32, device=dev)
         psteps = max(3, min(args.steps, 20))
-        pwall, pst, ptot = run_steps(moesq, torch, ev, px, torch.from_numpy(pids).to(dev),
-                                     torch.from_numpy(pwts).to(dev), [(w13, w2)], torch.from_numpy(pg13).to(dev),
-                                     torch.from_numpy(pg2).to(dev), pout, pws, min(args.warmup, 3), psteps)
+        pargs = (moesq, torch, ev, px, torch.from_numpy(pids).to(dev), torch.from_numpy(pwts).to(dev), [(w13, w2)],
+                 torch.from_numpy(pg13).to(dev), torch.from_numpy(pg2).to(dev), pout, pws, min(args.warmup, 3), psteps)
+        pwall, _, _ = run_steps(*pargs)
+        _, pst, _ = run_steps(*pargs, staged=True)
         PP = int((pids >= 0).sum())
         eff = 6.0 * PP * pw.H * pw.I / (pwall / psteps) / 1e12
         pst_mean = pst.mean(axis=0)
-        g_ms = float(pst_mean[2])
+        g_ms = float(pst_mean[moesq.FFN_STAGES.index("gemm_gate_up")])
         alg_flops = 2.0 * PP * (2 * pw.I) * pw.H / 2          # multiply-adds on the kept half of W13
         ach = alg_flops / (g_ms * 1e-3) / 1e12
         log("prefill stage ms (mean): " + ", ".join(f"{n}={v:.3f}ms" for n, v in zip(moesq.FFN_STAGES, pst_mean)))

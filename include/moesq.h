@@ -7,8 +7,9 @@
  * with MOESQ_FLAG_SYNC_CHECK). The library never allocates or frees device memory in these calls and
  * keeps no pointer after return; the caller owns every buffer, including workspaces, and keeps it
  * alive until the stream work is done. No C++ exception crosses this boundary. The calls keep no
- * global mutable state apart from a one-time kernel attribute set-up and the thread-local text of
- * moesq_last_error(), so they are reentrant.
+ * global mutable state apart from a one-time kernel attribute set-up and two thread-local values
+ * (the text of moesq_last_error() and the profiling events of moesq_set_stage_events()), so they
+ * are reentrant.
  *
  * Errors: a synchronous argument check returns a negative moesq_status and enqueues nothing; a launch
  * failure returns MOESQ_ERR_HIP with the HIP error text in moesq_last_error().
@@ -36,7 +37,7 @@
 extern "C" {
 #endif
 
-#define MOESQ_ABI_VERSION 2
+#define MOESQ_ABI_VERSION 3
 /* quantization_config marker "paired48_sparse": {"layout": "pair-bitmask", "version": 1} */
 #define MOESQ_PAIR_BITMASK_VERSION 1
 
@@ -105,10 +106,13 @@ moesq_status moesq_quantize_act(const void *x, moesq_dtype x_dtype, int64_t rows
  *            counted in *status).
  *   counts [E], offsets [E+1] (exclusive prefix of counts), sorted [T*k] (the offsets[E] live pair ids
  *   in (expert, p) order; the tail is not written), inv [T*k] (row of pair p, -1 if dropped),
- *   status [1] int32 (count of ids outside [-1, E)). E in [1, 1024], k in [1, 32]. */
+ *   status [1] int32 (count of ids outside [-1, E)). E in [1, 1024], k in [1, 32].
+ *   workspace: moesq_permute_workspace_size(T, E) bytes of device scratch (0 for T <= 512, where
+ *   workspace may be NULL). */
+size_t moesq_permute_workspace_size(int64_t T, int32_t E);
 moesq_status moesq_permute(const int32_t *topk_ids, int64_t T, int32_t k, int32_t E, int32_t *counts,
                            int32_t *offsets, int32_t *sorted, int32_t *inv, int32_t *status,
-                           hipStream_t stream);
+                           void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Grouped sparse GEMM (model card "Qwen3.5-397B-A17B-P48NVFP4-MoESQ": paired-4:8 sparse NVFP4
  * grouped GEMM over the routed experts): for each expert e and row r in [offsets[e], offsets[e+1]):
@@ -131,12 +135,14 @@ moesq_status moesq_grouped_gemm(const uint8_t *a_codes, const uint8_t *a_scales,
  *   silu(v) = v / (1 + exp(-v)); h is kept in fp32 before its quantization.
  *   out [T][H] fp32, overwritten. H % 256 == 0, I % 256 == 0.
  *   workspace: moesq_moe_ffn_workspace_size(...) bytes. After the call (stream order) it holds the
- *   intermediates at the offsets moesq_moe_ffn_layout() reports: counts, offsets, sorted, inv, the
- *   gate/up input codes+scales a13 and the down input codes+scales a2 (rows in sorted order), and the
- *   per-row down outputs (already times the router weight). */
+ *   intermediates at the offsets moesq_moe_ffn_layout() reports: counts, offsets, sorted, inv (as
+ *   moesq_permute writes them), the gate/up input codes+scales a13 in pair order (row p = t*k + j,
+ *   rows of dropped pairs unwritten), the down input codes+scales a2 and the per-row down outputs
+ *   (already times the router weight) in sorted order (row inv[p]); route_scratch is the
+ *   permutation's scratch. */
 typedef struct {
   size_t counts, offsets, tile_offsets, sorted, inv, status;
-  size_t a13_codes, a13_scales, a2_codes, a2_scales, down_rows;
+  size_t a13_codes, a13_scales, a2_codes, a2_scales, down_rows, route_scratch;
   size_t total;
   int32_t rows_per_mblock;   /* m-block size of the tactic the call uses */
 } moesq_ffn_layout;
@@ -149,10 +155,10 @@ moesq_status moesq_moe_ffn(const void *x, int64_t T, int32_t H, const int32_t *t
                            float *out, void *workspace, size_t workspace_bytes, uint32_t flags,
                            hipStream_t stream);
 
-/* Profiling aid: with events (host array of n >= 6 hipEvent_t created by the caller) set, every later
+/* Profiling aid: with events (host array of n >= 5 hipEvent_t created by the caller) set, every later
  * moesq_moe_ffn call on this host thread records events[0] on its stream before its first kernel and
- * events[1..5] after the permutation, the gate/up input quantization, the gate/up GEMM (with the
- * fused SiLU*up and down-input quantization), the down GEMM and the top-k combine. NULL disables it.
+ * events[1..4] after the routing (permutation and gate/up input quantization), the gate/up GEMM (with
+ * the fused SiLU*up and down-input quantization), the down GEMM and the top-k combine. NULL disables it.
  * The library keeps the pointer (thread-local) until it is reset; the caller keeps the array alive. */
 moesq_status moesq_set_stage_events(hipEvent_t *events /* host */, int32_t n);
 

@@ -33,7 +33,7 @@ EXPORTED_SYMBOLS = (
     "moesq_grouped_gemm_workspace_size", "moesq_grouped_gemm", "moesq_moe_ffn_layout",
     "moesq_moe_ffn_workspace_size", "moesq_moe_ffn", "moesq_compress_weights", "moesq_validate_weights",
     "moesq_unpack_pair_bitmask", "moesq_pack_pair_bitmask", "moesq_set_stage_events", "moesq_tiled_bytes",
-    "moesq_prepare_weights", "moesq_unprepare_weights",
+    "moesq_prepare_weights", "moesq_unprepare_weights", "moesq_permute_workspace_size",
 )
 
 
@@ -54,7 +54,7 @@ LAYOUT_TILED = 1
 class _CLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in ("counts", "offsets", "tile_offsets", "sorted", "inv", "status",
                                                 "a13_codes", "a13_scales", "a2_codes", "a2_scales",
-                                                "down_rows", "total")] + [("rows_per_mblock", ctypes.c_int32)]
+                                                "down_rows", "route_scratch", "total")] + [("rows_per_mblock", ctypes.c_int32)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -67,7 +67,8 @@ def _declare(L: ctypes.CDLL) -> None:
         "moesq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "moesq_last_error": (ctypes.c_char_p, []),
         "moesq_quantize_act": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I32, _I64, _P, _P, _I32, _P, _P, _P, _P]),
-        "moesq_permute": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P]),
+        "moesq_permute_workspace_size": (_SZ, [_I64, _I32]),
+        "moesq_permute": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
         "moesq_grouped_gemm_workspace_size": (_SZ, [_I32]),
         "moesq_grouped_gemm": (ctypes.c_int, [_P, _P, _P, _P, _I64, ctypes.POINTER(_CWeights), _P, _P, _SZ, _P]),
         "moesq_moe_ffn_layout": (ctypes.c_int, [_I64, _I32, _I32, _I32, _I32, _U32, ctypes.POINTER(_CLayout)]),
@@ -229,9 +230,11 @@ def permute(topk_ids: torch.Tensor, E: int):
     sorted_ = torch.full((T * k,), -1, dtype=torch.int32, device=dev)
     inv = torch.empty(T * k, dtype=torch.int32, device=dev)
     status = torch.empty(1, dtype=torch.int32, device=dev)
+    ws_bytes = lib().moesq_permute_workspace_size(T, E)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     _check(lib().moesq_permute(_dev(topk_ids, "topk_ids", torch.int32), T, k, E, _dev(counts, "counts"),
                                _dev(offsets, "offsets"), _dev(sorted_, "sorted"), _dev(inv, "inv"),
-                               _dev(status, "status"), _stream()))
+                               _dev(status, "status"), _dev(ws, "workspace"), ws_bytes, _stream()))
     return counts, offsets, sorted_, inv, status
 
 
@@ -279,7 +282,8 @@ def moe_ffn(x: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.Tensor,
 
 
 def ffn_intermediates(workspace: torch.Tensor, T: int, H: int, I: int, k: int, E: int) -> dict:
-    """Views of the intermediates a moe_ffn call left in its workspace (stream-ordered after the call)."""
+    """Views of the intermediates a moe_ffn call left in its workspace (stream-ordered after the call).
+    a13 rows are in pair order (row p = t*k + j); a2 and down rows in sorted order (row inv[p])."""
     L = ffn_layout(T, H, I, k, E)
     P = T * k
 
@@ -337,12 +341,12 @@ def compress_moe_layer(E: int, H: int, I: int, dense_expert, device="cuda"):
 
 
 #: Stages of one moe_ffn call, in the order set_stage_events() brackets them.
-FFN_STAGES = ("permute", "quantize_x", "gemm_gate_up", "gemm_down", "combine")
+FFN_STAGES = ("route", "gemm_gate_up", "gemm_down", "combine")
 
 
 def set_stage_events(events) -> None:
     """Record HIP events around the stages of later moe_ffn calls on this thread: ``events`` is a
-    ctypes array of >= 6 hipEvent_t handles (None disables)."""
+    ctypes array of >= len(FFN_STAGES) + 1 hipEvent_t handles (None disables)."""
     if events is None:
         _check(lib().moesq_set_stage_events(None, 0))
     else:

@@ -80,7 +80,7 @@ const char* moesq_status_string(moesq_status s) {
 const char* moesq_last_error(void) { return g_last_error.c_str(); }
 
 moesq_status moesq_set_stage_events(hipEvent_t* events, int32_t n) {
-  MOESQ_REQUIRE(!events || n >= 6, MOESQ_ERR_INVALID, "set_stage_events: need at least 6 events");
+  MOESQ_REQUIRE(!events || n >= 5, MOESQ_ERR_INVALID, "set_stage_events: need at least 5 events");
   g_stage_events = events;
   return MOESQ_OK;
 }
@@ -98,20 +98,28 @@ moesq_status moesq_quantize_act(const void* x, moesq_dtype x_dtype, int64_t rows
   MOESQ_REQUIRE((x_row_stride * (x_dtype == MOESQ_F32 ? 4 : 2)) % 16 == 0, MOESQ_ERR_INVALID,
                 "quantize_act: x row stride must be a multiple of 16 bytes");
   MOESQ_REQUIRE(!expert_offsets || E >= 1, MOESQ_ERR_INVALID, "quantize_act: E >= 1 with expert_offsets");
-  moesq::launch_quantize(x, x_dtype == MOESQ_F32, rows, K, x_row_stride, src_row, expert_offsets, E, nullptr,
-                         nullptr, nullptr, 1, global, codes, scales,
-                         expert_offsets ? moesq::kQuantOffsets : moesq::kQuantSingle, stream);
+  moesq::launch_quantize(x, x_dtype == MOESQ_F32, rows, K, x_row_stride, src_row, expert_offsets, E, global, codes,
+                         scales, stream);
   return check_launch(stream, false);
 }
 
+size_t moesq_permute_workspace_size(int64_t T, int32_t E) {
+  if (T < 0 || E < 1) return 0;
+  return moesq::route_scratch_bytes(T, E);
+}
+
 moesq_status moesq_permute(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E, int32_t* counts, int32_t* offsets,
-                           int32_t* sorted, int32_t* inv, int32_t* status, hipStream_t stream) {
+                           int32_t* sorted, int32_t* inv, int32_t* status, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
   MOESQ_REQUIRE(T >= 0 && k >= 1 && k <= 32 && E >= 1, MOESQ_ERR_INVALID, "permute: T >= 0, 1 <= k <= 32, E >= 1");
   MOESQ_REQUIRE(E <= 1024, MOESQ_ERR_UNSUPPORTED, "permute: at most 1024 experts");
   MOESQ_REQUIRE(counts && offsets && status && (T == 0 || (topk_ids && sorted && inv)), MOESQ_ERR_INVALID,
                 "permute: null pointer");
   MOESQ_REQUIRE(T * k < (int64_t)1 << 31, MOESQ_ERR_UNSUPPORTED, "permute: T*k must fit in int32");
-  moesq::launch_permute(topk_ids, T, k, E, counts, offsets, sorted, inv, nullptr, 0, status, stream);
+  const size_t need = moesq::route_scratch_bytes(T, E);
+  MOESQ_REQUIRE(workspace_bytes >= need && (need == 0 || workspace), MOESQ_ERR_WORKSPACE, "permute: workspace too small");
+  moesq::launch_route(topk_ids, T, k, E, counts, offsets, nullptr, 0, sorted, inv, status, workspace, nullptr, 0,
+                      nullptr, nullptr, nullptr, stream);
   return check_launch(stream, false);
 }
 
@@ -130,7 +138,8 @@ moesq_status moesq_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
                 "grouped_gemm: workspace too small");
   MOESQ_REQUIRE(aligned16(out) && aligned16(a_codes) && ((uintptr_t)a_scales & 3) == 0, MOESQ_ERR_INVALID,
                 "grouped_gemm: out and a_codes must be 16-byte aligned, a_scales 4-byte aligned");
-  MOESQ_REQUIRE(rows * w->K / 2 < ((int64_t)1 << 40), MOESQ_ERR_UNSUPPORTED, "grouped_gemm: too many rows");
+  MOESQ_REQUIRE(rows * (w->K / 2) < ((int64_t)1 << 31), MOESQ_ERR_UNSUPPORTED,
+                "grouped_gemm: activation codes must stay below 2 GiB (32-bit buffer offsets)");
   const int tactic = ffn_tactic(rows, w->E, w->K, w->K);
   int32_t* tile_offsets = static_cast<int32_t*>(workspace);
   moesq::launch_tile_offsets(expert_offsets, w->E, moesq::tactic_rows_per_mblock(tactic), tile_offsets, stream);
@@ -162,6 +171,7 @@ moesq_status moesq_moe_ffn_layout(int64_t T, int32_t H, int32_t I, int32_t k, in
   L->a2_codes = take(P * (size_t)(I / 2));
   L->a2_scales = take(P * (size_t)(I / 32));
   L->down_rows = take(P * (size_t)H * 4);
+  L->route_scratch = take(moesq::route_scratch_bytes(T, E));
   L->total = off;
   L->rows_per_mblock = moesq::tactic_rows_per_mblock(ffn_tactic(T * k, E, H, I));
   return MOESQ_OK;
@@ -189,6 +199,8 @@ moesq_status moesq_moe_ffn(const void* x, int64_t T, int32_t H, const int32_t* t
                 "moe_ffn: shapes must be w13 [2I, H], w2 [H, I]");
   MOESQ_REQUIRE(I % 256 == 0 && H % 256 == 0, MOESQ_ERR_UNSUPPORTED, "moe_ffn: H and I must be multiples of 256");
   MOESQ_REQUIRE(T * k < ((int64_t)1 << 31), MOESQ_ERR_UNSUPPORTED, "moe_ffn: T*k must fit in int32");
+  MOESQ_REQUIRE(T * k * (H / 2) < ((int64_t)1 << 31), MOESQ_ERR_UNSUPPORTED,
+                "moe_ffn: gate/up input codes must stay below 2 GiB (32-bit buffer offsets)");
   if (T == 0) return MOESQ_OK;
   MOESQ_REQUIRE(x && topk_ids && topk_weights && a13_global && a2_global && out && workspace, MOESQ_ERR_INVALID,
                 "moe_ffn: null pointer");
@@ -212,26 +224,26 @@ moesq_status moesq_moe_ffn(const void* x, int64_t T, int32_t H, const int32_t* t
   const int tactic = ffn_tactic(T * k, E, H, I);
   const int64_t P = T * k;
 
+  // routing: permutation + gate/up input quantization (pair order)
   stage_event(0, stream);
-  moesq::launch_permute(topk_ids, T, k, E, counts, offsets, sorted, inv, tile_offsets, L.rows_per_mblock, status, stream);
+  moesq::launch_route(topk_ids, T, k, E, counts, offsets, tile_offsets, L.rows_per_mblock, sorted, inv, status,
+                      ws + L.route_scratch, static_cast<const uint16_t*>(x), H, a13_global, a13c, a13s, stream);
   stage_event(1, stream);
-  moesq::launch_quantize(x, false, P, H, H, nullptr, nullptr, E, sorted, topk_ids, offsets + E, k, a13_global, a13c,
-                         a13s, moesq::kQuantPairs, stream);
-  stage_event(2, stream);
+  // gate/up GEMM, row r reading activation row sorted[r]; fused silu * up and down-input quantization
   moesq::GemmParams g{};
   g.a_codes = a13c; g.a_scales = a13s; g.a_global = a13_global; g.offsets = offsets; g.tile_offsets = tile_offsets;
-  g.rows = P; g.w_packed = w13->packed; g.w_mask = w13->mask; g.w_scale = w13->scale; g.w_global = w13->global;
+  g.a_rows = sorted; g.rows = P; g.w_packed = w13->packed; g.w_mask = w13->mask; g.w_scale = w13->scale; g.w_global = w13->global;
   g.E = E; g.N = w13->N; g.K = H; g.G = 2; g.layout = w13->layout; g.h_codes = a2c; g.h_scales = a2s; g.h_global = a2_global;
   moesq::launch_grouped_gemm(g, moesq::kEpiGateUp, tactic, stream);
-  stage_event(3, stream);
+  stage_event(2, stream);
   moesq::GemmParams d{};
   d.a_codes = a2c; d.a_scales = a2s; d.a_global = a2_global; d.offsets = offsets; d.tile_offsets = tile_offsets;
   d.rows = P; d.w_packed = w2->packed; d.w_mask = w2->mask; d.w_scale = w2->scale; d.w_global = w2->global;
   d.E = E; d.N = H; d.K = I; d.G = 1; d.layout = w2->layout; d.out = drows; d.topk_weights = topk_weights; d.sorted = sorted;
   moesq::launch_grouped_gemm(d, moesq::kEpiDown, tactic, stream);
-  stage_event(4, stream);
+  stage_event(3, stream);
   moesq::launch_combine(drows, inv, T, k, H, out, stream);
-  stage_event(5, stream);
+  stage_event(4, stream);
   return check_launch(stream, (flags & MOESQ_FLAG_SYNC_CHECK) != 0);
 }
 

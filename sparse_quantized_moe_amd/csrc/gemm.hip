@@ -35,27 +35,51 @@ constexpr int kGemmThreads = 256;
 // ---------------------------------------------------------------------------------------------
 // Decode kernel
 // ---------------------------------------------------------------------------------------------
-constexpr int kDecLdsB = 32 * 1024;           // activation bytes staged in LDS at a time
+constexpr int kDecTG = 2;                       // token tiles per m-block
+constexpr int kDecBMT = kDecTG * 16;            // rows per m-block
+constexpr int kDecTPR = kGemmThreads / kDecBMT; // staging threads per row
+constexpr uint32_t kOutOfRange = 0x80000000u;   // a buffer offset past num_records: the load reads zero
 
-// K staged per chunk for TG token tiles (a multiple of 256).
-__host__ __device__ constexpr int dec_kc(int TG) { return kDecLdsB / (TG * 16 * 2); }
+// Staging geometry for a weight ring of DEPTH slots: one staged chunk = DEPTH 256-K super-steps.
+template <int DEPTH>
+struct DecGeom {
+  static constexpr int KC = DEPTH * 256;                 // K staged in LDS at a time
+  static constexpr int RS = KC * 2 + 16;                 // LDS bytes per token row (f16, +16 B skew)
+  static constexpr int IPT = KC / 32 / kDecTPR;          // consecutive 32-K groups per staging thread
+  static_assert(KC / 32 % kDecTPR == 0, "whole staging groups per thread");
+  static constexpr size_t lds = (size_t)kDecBMT * RS + 512;
+};
 
-// Position of local chunk c (0..31) of a super-step in LDS: c and c+16 sit side by side, so a B
-// lane's two chunks are one contiguous 32-byte read.
-__device__ __forceinline__ int dec_chunk_pos(int c) { return ((c & 15) << 1) | (c >> 4); }
+// Ring depth of a decode variant: gate/up waves (4 row-tiles) hold two weight super-steps in
+// registers, the others (2 row-tiles) three.
+__host__ __device__ constexpr int dec_depth(int rt) { return rt >= 4 ? 2 : 3; }
 
-// One workgroup per (expert, n-block): the expert comes straight from the block index, so the only
-// round trip before the weight stream starts is the read of the expert's row range; experts with
-// more than 32 rows are covered by further passes over the same (now cache-resident) weights.
+// Activation codes of one staged chunk, held in registers from one chunk ahead.
+template <int IPT>
+struct ActChunk {
+  u32x4 v[IPT];
+  uint32_t s[IPT];
+};
+
+// One workgroup per (expert, n-block): the expert comes straight from the block index. Experts with
+// more than kDecBMT rows take further passes over the same (cache-resident) weights.
+//
+// Every global load in the K loop is a prefetch: weights stream through a register ring of DEPTH
+// slots, each slot reloaded (DEPTH super-steps ahead) as soon as its last fragment word is decoded,
+// and the activation codes of the next chunk are loaded into registers while the current one is
+// used. vmcnt retires loads in order, so a synchronous load here would also wait for every weight
+// load in flight; with only prefetches, and every load issued on every path, each wait counts
+// exactly the loads issued after the data it needs.
 template <int EPI, int LAYOUT, int RT>
 __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(3))) void k_gemm_decode(GemmParams p) {
-  constexpr int TG = 2, BMT = TG * 16;
-  constexpr int KCMAX = dec_kc(TG);
-  constexpr int RS = KCMAX * 2 + 16;                              // LDS bytes per token row (+16 B skew)
+  constexpr int TG = kDecTG, BMT = kDecBMT, DEPTH = dec_depth(RT);
+  using Geo = DecGeom<DEPTH>;
+  constexpr int RS = Geo::RS, KC = Geo::KC, IPT = Geo::IPT;
   extern __shared__ __align__(16) uint8_t smem[];
   const int K = p.K;
-  uint8_t* sB = smem;                                             // [BMT][RS] f16, chunk pairs adjacent
+  uint8_t* sB = smem;                                             // [BMT][RS] f16
   uint16_t* lut_idx = reinterpret_cast<uint16_t*>(smem + BMT * RS);   // [256]
+  __shared__ int s_arow[BMT];                                     // activation row of each m-block row
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int e = blockIdx.x, nb = blockIdx.y;
@@ -69,53 +93,64 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(3)
   WeightPtrs<LAYOUT, RT> wp;
   wp.init(p, e, wrow, active, lane);
   const int nsteps = K >> 8;
-  constexpr int spc = KCMAX >> 8;                                 // super-steps per staged chunk
   const int nrow = lane & 15, qb = lane >> 4;
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.a_codes), (short)0, (int)(p.rows * (K >> 1)), kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.a_scales), (short)0, (int)(p.rows * (K >> 5)), kBufferRsrcWord3);
+  // staging map: thread -> row sn, 32-K groups sq0 .. sq0 + IPT - 1 of each chunk
+  const int sn = tid / kDecTPR, sq0 = (tid % kDecTPR) * IPT;
 
   for (int m0 = 0; m0 < M; m0 += BMT) {
     const int mrows = M - m0 < BMT ? M - m0 : BMT;
     const int ntiles = (mrows + 15) >> 4;
-    WeightFrag<RT> w0, w1, w2;
-    if (active) {
-      wp.load(0, w0);
-      if (nsteps > 1) wp.load(1, w1);
+    // every thread is past the previous m-block's last staging barrier, so s_arow is free
+    __syncthreads();
+    if (tid < BMT) {
+      const int r = row0 + m0 + tid;
+      s_arow[tid] = tid < mrows ? (p.a_rows ? p.a_rows[r] : r) : 0;
     }
+    __syncthreads();
+    // registers of the activation chunk [k0, k0 + kc): rows past the m-block and groups past the
+    // chunk get an out-of-range offset and read zero (no branch, no zero fill)
+    const bool srow_live = sn < mrows;
+    const uint32_t ar = (uint32_t)s_arow[srow_live ? sn : 0];
+    auto prefetch = [&](int k0, int kc, ActChunk<IPT>& ac) {
+      const int quads = kc >> 5;
+      const uint32_t cbase = ar * (uint32_t)(K >> 1) + (uint32_t)((k0 >> 1) + sq0 * 16);
+      const uint32_t sbase = ar * (uint32_t)(K >> 5) + (uint32_t)((k0 >> 5) + sq0);
+#pragma unroll
+      for (int j = 0; j < IPT; ++j) {
+        const bool live = srow_live && sq0 + j < quads;
+        ac.v[j] = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, live ? cbase + 16u * j : kOutOfRange, 0, 0);
+        ac.s[j] = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, live ? sbase + j : kOutOfRange, 0, 0);
+      }
+    };
+    // exact f16 values of the chunk into LDS in B-operand order (rows past the m-block as zeros,
+    // groups past the chunk into positions no step reads)
+    auto commit = [&](const ActChunk<IPT>& ac) {
+      __syncthreads();
+      if (sn < ntiles * 16) {
+#pragma unroll
+        for (int j = 0; j < IPT; ++j) {
+          const f16 sv = e4m3_to_f16(ac.s[j]);
+          const f16x2 s2 = f16x2{sv, sv};
+          const uint32_t wv4[4] = {ac.v[j].x, ac.v[j].y, ac.v[j].z, ac.v[j].w};
+#pragma unroll
+          for (int h = 0; h < 4; ++h)                               // 8-K chunk 4 (sq0 + j) + h
+            *reinterpret_cast<u32x4*>(sB + sn * RS + (4 * (sq0 + j) + h) * 16) = act_chunk_kprime(wv4[h], s2);
+        }
+      }
+      __syncthreads();
+    };
     f32x4 acc[RT][TG];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int tt = 0; tt < TG; ++tt) acc[rt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int64_t arow = (int64_t)(row0 + m0) * (K >> 1);
-    const int64_t srow = (int64_t)(row0 + m0) * (K >> 5);
-    auto step = [&](int gs, const WeightFrag<RT>& w) {
-      const int ssl = gs % spc;
-      if (ssl == 0) {
-        // stage the K-chunk [k0, k0 + kc) of the m-block's activations as exact f16
-        const int k0 = gs * 256;
-        const int kc = K - k0 < KCMAX ? K - k0 : KCMAX;
-        const int quads = kc >> 5;                                // 4-chunk groups (32 K) per row
-        __syncthreads();
-        for (int i = tid; i < ntiles * 16 * quads; i += kGemmThreads) {
-          const int n = i / quads, q4 = i - n * quads;
-          u32x4 v = u32x4{0u, 0u, 0u, 0u};
-          uint32_t sb = 0;
-          if (n < mrows) {
-            v = *reinterpret_cast<const u32x4*>(p.a_codes + arow + (int64_t)n * (K >> 1) + (k0 >> 1) + q4 * 16);
-            sb = p.a_scales[srow + (int64_t)n * (K >> 5) + (k0 >> 5) + q4];
-          }
-          const f16 s = e4m3_to_f16(sb);
-          const f16x2 s2 = f16x2{s, s};
-          const uint32_t wv4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int c = 4 * q4 + j;                             // chunk within the staged K-chunk
-            const int pos = (c & ~31) + dec_chunk_pos(c & 31);
-            *reinterpret_cast<u32x4*>(sB + n * RS + pos * 16) = act_chunk_kprime(wv4[j], s2);
-          }
-        }
-        __syncthreads();
-      }
-      if (!active) return;
+    // MFMAs of one super-step (position ssl of its chunk) on weight fragment w; once the last word
+    // of w is decoded, w is reloaded with super-step `reload` (< 0: none)
+    auto step = [&](int ssl, WeightFrag<RT>& w, int reload) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         f16x8 A[RT];
@@ -127,13 +162,14 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(3)
           A[rt] = weight_operand_of<LAYOUT>(frag_word(w.pk[rt], t), s2);
           idx[rt] = lut_idx[(w.mk[rt] >> (8 * t)) & 255u];
         }
+        if (t == 3 && reload >= 0) wp.load(reload, w, active && reload < nsteps);
         const int c0 = 8 * (qb >> 1) + 2 * t + (qb & 1);
 #pragma unroll
         for (int tt = 0; tt < TG; ++tt) {
           if (tt < ntiles) {
-            const uint8_t* bp = sB + (tt * 16 + nrow) * RS + (32 * ssl + 2 * c0) * 16;
+            const uint8_t* bp = sB + (tt * 16 + nrow) * RS + (32 * ssl + c0) * 16;
             const u32x4 b0 = *reinterpret_cast<const u32x4*>(bp);
-            const u32x4 b1 = *reinterpret_cast<const u32x4*>(bp + 16);
+            const u32x4 b1 = *reinterpret_cast<const u32x4*>(bp + 16 * 16);
             const f16x16 B = __builtin_bit_cast(f16x16, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
@@ -142,19 +178,26 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(3)
         }
       }
     };
-    // Three-slot register ring, unrolled by its period so no register of a load in flight is ever
-    // copied: step gs reads slot gs % 3 while the loads of gs + 1 and gs + 2 are outstanding.
+    ActChunk<IPT> ac;
+    prefetch(0, K < KC ? K : KC, ac);
+    WeightFrag<RT> w[DEPTH];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) wp.load(d, w[d], active && d < nsteps);
+    // One chunk per iteration, its DEPTH super-steps on the DEPTH ring slots.
     int gs = 0;
-    for (; gs + 3 <= nsteps; gs += 3) {
-      if (active && gs + 2 < nsteps) wp.load(gs + 2, w2);
-      step(gs, w0);
-      if (active && gs + 3 < nsteps) wp.load(gs + 3, w0);
-      step(gs + 1, w1);
-      if (active && gs + 4 < nsteps) wp.load(gs + 4, w1);
-      step(gs + 2, w2);
+    for (; gs + DEPTH <= nsteps; gs += DEPTH) {
+      const int k1 = (gs + DEPTH) * 256;
+      commit(ac);
+      prefetch(k1, K - k1 < KC ? K - k1 : KC, ac);
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) step(d, w[d], gs + DEPTH + d);
     }
-    if (gs < nsteps) step(gs, w0);
-    if (gs + 1 < nsteps) step(gs + 1, w1);
+    if (gs < nsteps) {                                            // a last, shorter chunk
+      commit(ac);
+#pragma unroll
+      for (int d = 0; d < DEPTH - 1; ++d)
+        if (gs + d < nsteps) step(d, w[d], -1);
+    }
     if (active) gemm_epilogue<EPI, TG, RT>(p, acc, e, row0, m0, mrows, nb, wv, wrow, lane);
   }
 }
@@ -173,6 +216,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_prefill(GemmParams p) {
   uint8_t* sB = smem;
   uint16_t* lut = reinterpret_cast<uint16_t*>(smem + kPreLdsB);
   __shared__ int s_e;
+  __shared__ int s_arow[kPreBMT];                 // activation row of each m-block row
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int mb = blockIdx.x, nb = blockIdx.y;
@@ -184,6 +228,10 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_prefill(GemmParams p) {
   const int M = p.offsets[e + 1] - row0;
   const int m0 = (mb - p.tile_offsets[e]) * kPreBMT;
   const int mrows = M - m0 < kPreBMT ? M - m0 : kPreBMT;
+  if (tid < kPreBMT) {                            // read after the first step's barrier
+    const int r = row0 + m0 + tid;
+    s_arow[tid] = tid < mrows ? (p.a_rows ? p.a_rows[r] : r) : 0;
+  }
 
   int wrow[4];
   const bool active = wave_rows<EPI>(p.N, nb, wv, wrow);
@@ -209,7 +257,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_prefill(GemmParams p) {
       const int n = i >> 5, c = i & 31;
       u32x4 v = u32x4{0u, 0u, 0u, 0u};
       if (n < mrows) {
-        const int64_t ar = row0 + m0 + n;
+        const int64_t ar = s_arow[n];
         const uint32_t codes = *reinterpret_cast<const uint32_t*>(p.a_codes + ar * a_row_bytes + ((k0 >> 3) + c) * 4);
         const uint32_t sb = p.a_scales[ar * a_row_scales + ((k0 >> 5) + (c >> 2))];
         const f16 s = e4m3_to_f16(sb);
@@ -258,13 +306,12 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_prefill(GemmParams p) {
   gemm_epilogue<EPI, kPreTG>(p, acc, e, row0, m0, mrows, nb, wv, wrow, lane);
 }
 
-constexpr int kDecTG = 2;                     // token tiles per decode m-block
-
 int tactic_rows_per_mblock(int tactic) { return tactic == kTacticPrefill ? kPreBMT : kDecTG * 16; }
 
 size_t gemm_lds_bytes(int tactic, int K) {
   (void)K;
-  return tactic == kTacticPrefill ? (size_t)kPreLdsB + 512 : (size_t)kDecTG * 16 * (dec_kc(kDecTG) * 2 + 16) + 512;
+  // the decode tactic's largest variant (the deepest ring)
+  return tactic == kTacticPrefill ? (size_t)kPreLdsB + 512 : DecGeom<3>::lds;
 }
 
 template <class Kern>
@@ -281,7 +328,7 @@ static void launch_decode(const GemmParams& p, hipStream_t stream) {
   // gate/up waves own 4 row-tiles (32 columns for the fused quantization); other linears stream
   // 2 row-tiles per wave, which keeps more, shorter streams in flight for short K
   constexpr int RT = EPI == kEpiGateUp ? 4 : 2;
-  const size_t lds = gemm_lds_bytes(kTacticDecode, p.K);
+  const size_t lds = DecGeom<dec_depth(RT)>::lds;
   set_lds_attr(&k_gemm_decode<EPI, LAYOUT, RT>, lds);
   const int nblocks = EPI == kEpiGateUp ? ((p.N >> 1) + 127) / 128 : (p.N + 64 * RT - 1) / (64 * RT);
   k_gemm_decode<EPI, LAYOUT, RT><<<dim3((unsigned)p.E, (unsigned)nblocks), kGemmThreads, lds, stream>>>(p);

@@ -45,32 +45,55 @@ struct WeightPtrs<0, RT> {
       w.sc[rt] = *reinterpret_cast<const uint16_t*>(sc[rt] + 8 * gs);
     }
   }
+
+  // live = false: zeros instead of a load
+  __device__ __forceinline__ void load(int gs, WeightFrag<RT>& w, bool live) const {
+    if (live) {
+      load(gs, w);
+    } else {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        w.pk[rt] = u32x4{0u, 0u, 0u, 0u};
+        w.mk[rt] = 0u;
+        w.sc[rt] = 0u;
+      }
+    }
+  }
 };
+
+// A lane index whose record offsets (2, 4 or 16 bytes per lane) all lie at or past 2^31, beyond
+// any buffer's num_records.
+constexpr uint32_t kOutOfRangeLanes = 0x08000000u;
 
 template <int RT>
 struct WeightPtrs<1, RT> {
-  const uint8_t* base[RT];  // wave-uniform record pointer of each row-tile's first step
-  int lane16;               // lane offsets inside a record
+  __amdgpu_buffer_rsrc_t rsrc;  // the expert's records (wave-uniform, scalar registers)
+  int tile_off[RT];             // byte offset of each row-tile's first record in the expert (uniform)
+  uint32_t lane;                // lane offsets inside a record: 16 lane, 1024 + 4 lane, 1280 + 2 lane
 
-  __device__ __forceinline__ void init(const GemmParams& p, int e, const int* wrow, bool active, int lane) {
+  __device__ __forceinline__ void init(const GemmParams& p, int e, const int* wrow, bool active, int ln) {
     const int steps = p.K >> 8;
+    const int64_t expert_bytes = (int64_t)(p.N >> 4) * steps * kTileRecordBytes;
+    rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.w_packed) + e * expert_bytes, (short)0,
+                                             (int)expert_bytes, kBufferRsrcWord3);
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const int r = __builtin_amdgcn_readfirstlane(active ? wrow[rt] : 0);
-      const int64_t tile = (int64_t)e * (p.N >> 4) + (r >> 4);
-      base[rt] = p.w_packed + tile * steps * kTileRecordBytes;
-    }
-    lane16 = lane;
+    for (int rt = 0; rt < RT; ++rt)
+      tile_off[rt] = __builtin_amdgcn_readfirstlane(active ? (wrow[rt] >> 4) : 0) * steps * kTileRecordBytes;
+    lane = (uint32_t)ln;
   }
 
-  __device__ __forceinline__ void load(int gs, WeightFrag<RT>& w) const {
-    const int64_t off = (int64_t)gs * kTileRecordBytes;
+  __device__ __forceinline__ void load(int gs, WeightFrag<RT>& w) const { load(gs, w, true); }
+
+  // live = false: the same loads at an offset past the buffer, which read zeros without touching
+  // memory (keeps the number of loads in flight the same on every path)
+  __device__ __forceinline__ void load(int gs, WeightFrag<RT>& w, bool live) const {
+    const uint32_t l = lane + (live ? 0u : kOutOfRangeLanes);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      const uint8_t* rec = base[rt] + off;
-      w.pk[rt] = *reinterpret_cast<const u32x4*>(rec + 16 * lane16);
-      w.mk[rt] = *reinterpret_cast<const uint32_t*>(rec + kTileMaskOffset + 4 * lane16);
-      w.sc[rt] = *reinterpret_cast<const uint16_t*>(rec + kTileScaleOffset + 2 * lane16);
+      const int soff = tile_off[rt] + gs * kTileRecordBytes;
+      w.pk[rt] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, l * 16u, soff, 0);
+      w.mk[rt] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, l * 4u + kTileMaskOffset, soff, 0);
+      w.sc[rt] = __builtin_amdgcn_raw_buffer_load_b16(rsrc, l * 2u + kTileScaleOffset, soff, 0);
     }
   }
 };

@@ -201,4 +201,8 @@ constexpr int kTileRecordBytes = 1408;
 constexpr int kTileMaskOffset = 1024;
 constexpr int kTileScaleOffset = 1280;
 
+// Word 3 of a raw buffer resource on gfx9-family targets (gfx950): no format conversion, no swizzle;
+// an access past num_records bytes reads zero.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
 }  // namespace moesq

@@ -5,12 +5,11 @@
 
 namespace moesq {
 
-enum { kQuantSingle = 0, kQuantOffsets = 1, kQuantPairs = 2 };
-
+// Rows of x (gathered through src_row when given) quantized with global[0], or with global[e] for
+// the rows offsets[e] .. offsets[e+1] when offsets is given.
 void launch_quantize(const void* x, bool f32, int64_t rows, int K, int64_t stride, const int* src_row,
-                     const int* offsets, int E, const int* pair_of_row, const int* pair_expert,
-                     const int* row_limit, int k, const float* global, uint8_t* codes, uint8_t* scales,
-                     int mode, hipStream_t stream);
+                     const int* offsets, int E, const float* global, uint8_t* codes, uint8_t* scales,
+                     hipStream_t stream);
 void launch_compress(const float* w, int64_t N, int K, uint8_t* packed, uint8_t* mask, uint8_t* scale,
                      float* global, hipStream_t stream);
 void launch_validate(const uint8_t* mask, int64_t nbytes, int* bad, hipStream_t stream);
@@ -27,11 +26,15 @@ void launch_prepare(const uint8_t* packed, const uint8_t* mask, const uint8_t* s
 void launch_unprepare(const uint8_t* tiled, int E, int N, int K, uint8_t* packed, uint8_t* mask, uint8_t* scale,
                       hipStream_t stream);
 
-// Permutation: counts[E], offsets[E+1], sorted[T*k] (live prefix), inv[T*k], tile_offsets[E+1]
-// (prefix of ceil(count/bm) for the grouped GEMM's m-blocks, when bm > 0) and status[0] (number of
-// ids outside [-1, E), which are dropped).
-void launch_permute(const int* ids, int64_t T, int k, int E, int* counts, int* offsets, int* sorted,
-                    int* inv, int* tile_offsets, int bm, int* status, hipStream_t stream);
+// Routing: counts[E], offsets[E+1], sorted[T*k] (live prefix), inv[T*k], tile_offsets[E+1] (prefix
+// of ceil(count/bm) for the grouped GEMM's m-blocks, when bm > 0) and status[0] (number of ids
+// outside [-1, E), which are dropped); with x (bf16 [T][H]) also the NVFP4 codes [T*k][H/2] and
+// scales [T*k][H/32] of every live pair p, row p, with global a_global[ids[p]]. scratch holds
+// route_scratch_bytes(T, E) bytes (none for T <= 512).
+size_t route_scratch_bytes(int64_t T, int E);
+void launch_route(const int* ids, int64_t T, int k, int E, int* counts, int* offsets, int* tile_offsets, int bm,
+                  int* sorted, int* inv, int* status, void* scratch, const uint16_t* x, int H, const float* a_global,
+                  uint8_t* codes, uint8_t* scales, hipStream_t stream);
 // tile_offsets from offsets for m-blocks of bm rows.
 void launch_tile_offsets(const int* offsets, int E, int bm, int* tile_offsets, hipStream_t stream);
 
@@ -44,12 +47,14 @@ size_t gemm_lds_bytes(int tactic, int K);
 constexpr size_t kMaxLdsBytes = 160 * 1024;
 
 struct GemmParams {
-  // B operand: activation codes [rows][K/2], scales [rows][K/32]; expert e owns rows offsets[e]..
+  // B operand: activation codes [.][K/2], scales [.][K/32]; expert e owns GEMM rows offsets[e]..
+  // offsets[e+1]-1, and GEMM row r reads activation row a_rows[r] (row r itself when a_rows is null)
   const uint8_t* a_codes;
   const uint8_t* a_scales;
   const float* a_global;     // [E]
   const int* offsets;        // [E+1]
   const int* tile_offsets;   // [E+1], m-blocks of tactic_rows_per_mblock rows
+  const int* a_rows;         // [rows] or null
   int64_t rows;              // rows of A (upper bound of offsets[E])
   // weights, pair-bitmask storage [E][N][K/4], [E][N][K/16], [E][N][K/32], global [E][G]
   const uint8_t* w_packed;

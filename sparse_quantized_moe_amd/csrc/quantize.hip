@@ -19,14 +19,9 @@ struct QuantArgs {
   int64_t rows;
   int K;
   int64_t stride;          // elements between rows of x
-  // row -> source row of x and expert (one of three modes)
-  const int* src_row;      // mode OFFSETS / IDENTITY: source row (NULL = identity)
-  const int* offsets;      // mode OFFSETS: [E+1], binary search; NULL = a single global
+  const int* src_row;      // source row of x per row (NULL = identity)
+  const int* offsets;      // [E+1]: rows offsets[e] .. offsets[e+1]-1 use global[e] (binary search)
   int E;
-  const int* pair_of_row;  // mode PAIRS: sorted pair id p of the row; x row = p / k, expert = ids[p]
-  const int* pair_expert;  //   topk ids [T*k]
-  const int* row_limit;    //   rows >= *row_limit are skipped (the live pair count)
-  int k;
   const float* global;
   uint8_t* codes;
   uint8_t* scales;
@@ -71,33 +66,25 @@ __device__ __forceinline__ uint32_t quantize_group(const float v[32], float g, u
   return (uint32_t)sc;
 }
 
-template <bool F32, int MODE>
+template <bool F32, bool OFFSETS>
 __global__ __launch_bounds__(256) void k_quantize(QuantArgs a) {
   const int G = a.K >> 5;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t r = gid / G;
   const int grp = (int)(gid - r * G);
   if (r >= a.rows) return;
-  int64_t src;
+  const int64_t src = a.src_row ? a.src_row[r] : r;
   float g;
-  if (MODE == kQuantPairs) {
-    if (r >= *a.row_limit) return;
-    const int p = a.pair_of_row[r];
-    src = p / a.k;
-    g = a.global[a.pair_expert[p]];
-  } else {
-    src = a.src_row ? a.src_row[r] : r;
-    if (MODE == kQuantOffsets) {
-      int lo = 0, hi = a.E;                       // largest e with offsets[e] <= r
-      if (r >= a.offsets[a.E] || r < a.offsets[0]) return;
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (a.offsets[mid] <= r) lo = mid; else hi = mid;
-      }
-      g = a.global[lo];
-    } else {
-      g = a.global[0];
+  if (OFFSETS) {
+    int lo = 0, hi = a.E;                         // largest e with offsets[e] <= r
+    if (r >= a.offsets[a.E] || r < a.offsets[0]) return;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (a.offsets[mid] <= r) lo = mid; else hi = mid;
     }
+    g = a.global[lo];
+  } else {
+    g = a.global[0];
   }
   float v[32];
   load_group<F32>(a.x, src * a.stride + (int64_t)grp * 32, v);
@@ -108,21 +95,18 @@ __global__ __launch_bounds__(256) void k_quantize(QuantArgs a) {
 }
 
 void launch_quantize(const void* x, bool f32, int64_t rows, int K, int64_t stride, const int* src_row,
-                     const int* offsets, int E, const int* pair_of_row, const int* pair_expert,
-                     const int* row_limit, int k, const float* global, uint8_t* codes, uint8_t* scales,
-                     int mode, hipStream_t stream) {
-  QuantArgs a{x, rows, K, stride, src_row, offsets, E, pair_of_row, pair_expert, row_limit, k, global, codes, scales};
+                     const int* offsets, int E, const float* global, uint8_t* codes, uint8_t* scales,
+                     hipStream_t stream) {
+  QuantArgs a{x, rows, K, stride, src_row, offsets, E, global, codes, scales};
   const int64_t n = rows * (K >> 5);
   if (n == 0) return;
   const dim3 grid((unsigned)((n + 255) / 256));
   if (f32) {
-    if (mode == kQuantPairs) k_quantize<true, kQuantPairs><<<grid, 256, 0, stream>>>(a);
-    else if (mode == kQuantOffsets) k_quantize<true, kQuantOffsets><<<grid, 256, 0, stream>>>(a);
-    else k_quantize<true, kQuantSingle><<<grid, 256, 0, stream>>>(a);
+    if (offsets) k_quantize<true, true><<<grid, 256, 0, stream>>>(a);
+    else k_quantize<true, false><<<grid, 256, 0, stream>>>(a);
   } else {
-    if (mode == kQuantPairs) k_quantize<false, kQuantPairs><<<grid, 256, 0, stream>>>(a);
-    else if (mode == kQuantOffsets) k_quantize<false, kQuantOffsets><<<grid, 256, 0, stream>>>(a);
-    else k_quantize<false, kQuantSingle><<<grid, 256, 0, stream>>>(a);
+    if (offsets) k_quantize<false, true><<<grid, 256, 0, stream>>>(a);
+    else k_quantize<false, false><<<grid, 256, 0, stream>>>(a);
   }
 }
 

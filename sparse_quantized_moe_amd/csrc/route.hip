@@ -1,0 +1,336 @@
+// Routing front of the MoE FFN: the stable token -> expert permutation and the NVFP4 quantization of
+// every (token, expert) pair's activation row, in one launch when the tokens fit one tile.
+//
+// Permutation (the grouped GEMM of model card "Qwen3.5-397B-A17B-P48NVFP4-MoESQ" runs one GEMM per
+// expert over that expert's rows): pairs p = t*k + j are grouped by expert, stable in p. Tokens are cut
+// into tiles of 512, one workgroup each. Inside a tile every wave of 64 tokens sets, per expert, the
+// bits of its lanes in a 64-bit LDS mask, and the rank of a pair inside the tile is
+//   (pairs of e in earlier waves of the tile) + popcount(mask[e] & lanes below).
+// That is the stable order because a token names each expert at most once; a tile holding a token
+// that names an expert twice (detected by the mask bit being set already) is ranked serially by one
+// thread instead, giving the same order. The row of a pair is then
+//   offsets[e] + (pairs of e in earlier tiles) + rank in the tile.
+// With one tile, its workgroup also scans and scatters. With several, a scan kernel and a scatter
+// kernel follow. Ids outside [-1, E) are dropped like -1 and counted in status[0].
+//
+// Quantization (model card "Compression details": NVFP4 activations with per-32 scales and an FP32
+// global stored per expert linear): row p of the codes is NVFP4(x[t], a_global[ids[p]]) in pair order,
+// so it does not wait for the permutation; the GEMM reads row sorted[r] for its r-th row. A thread
+// loads one 32-group of a token once, takes its amax once and encodes it for a run of that token's
+// experts.
+#include "moesq_device.h"
+#include "moesq_internal.h"
+
+namespace moesq {
+
+constexpr int kRouteThreads = 512;
+constexpr int kRouteWaves = kRouteThreads / 64;
+
+// Exclusive scan in place of a[0..n) (LDS) by the whole workgroup; returns the total.
+__device__ int route_block_scan(int* a, int n, int* tmp) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int per = (n + kRouteThreads - 1) / kRouteThreads;
+  const int s0 = tid * per < n ? tid * per : n;
+  const int s1 = s0 + per < n ? s0 + per : n;
+  int sum = 0;
+  for (int i = s0; i < s1; ++i) sum += a[i];
+  int v = sum;                                   // inclusive scan over the wave
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int u = __shfl_up(v, off);
+    if (lane >= off) v += u;
+  }
+  if (lane == 63) tmp[wv] = v;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int w = 0; w < kRouteWaves; ++w) { const int x = tmp[w]; tmp[w] = run; run += x; }
+    tmp[kRouteWaves] = run;
+  }
+  __syncthreads();
+  int base = tmp[wv] + v - sum;
+  const int total = tmp[kRouteWaves];
+  for (int i = s0; i < s1; ++i) {
+    const int x = a[i];
+    a[i] = base;
+    base += x;
+  }
+  __syncthreads();
+  return total;
+}
+
+struct RouteArgs {
+  const int* ids;            // [T*k]
+  int64_t T;
+  int k, E, ntiles;
+  int* counts;               // [E]
+  int* offsets;              // [E+1]
+  int* tile_offsets;         // [E+1] prefix of ceil(count / bm), when bm > 0
+  int bm;
+  int* sorted;               // [T*k], live prefix offsets[E]
+  int* inv;                  // [T*k]; holds the in-tile rank until the scatter
+  int* status;               // [1]
+  int* tile_counts;          // several tiles: [ntiles][E] counts, then [ntiles] dropped-id counts
+  // quantization of the pairs' rows (qblocks = 0: none)
+  const uint16_t* x;         // bf16 [T][H]
+  int H;
+  const float* a_global;     // [E]
+  uint8_t* codes;            // [T*k][H/2]
+  uint8_t* scales;           // [T*k][H/32]
+  int qblocks;
+  int kchunk;                // experts encoded per thread
+};
+
+__device__ void route_tile(const RouteArgs& a, int tile, uint8_t* smem) {
+  const int E = a.E, k = a.k;
+  unsigned long long* wmask = reinterpret_cast<unsigned long long*>(smem);   // [waves][E]
+  int* wbase = reinterpret_cast<int*>(wmask + kRouteWaves * E);              // [waves][E]
+  int* cnt = wbase + kRouteWaves * E;                                         // [E]
+  int* tcnt = cnt + E;                                                        // [E]
+  __shared__ int tmp[kRouteWaves + 1];
+  __shared__ int s_bad, s_dup;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t t = (int64_t)tile * kRouteThreads + tid;
+  const bool valid = t < a.T;
+  const unsigned long long bit = 1ull << lane, below = bit - 1ull;
+
+  for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) wmask[i] = 0ull;
+  if (tid == 0) { s_bad = 0; s_dup = 0; }
+  __syncthreads();
+  if (valid) {
+    int bad = 0, dup = 0;
+    for (int j = 0; j < k; ++j) {
+      const int e = a.ids[t * k + j];
+      if (e < 0 || e >= E) { bad += e != -1; continue; }
+      const unsigned long long old = atomicOr(&wmask[wv * E + e], bit);
+      dup |= (old & bit) != 0ull;
+    }
+    if (bad) atomicAdd(&s_bad, bad);
+    if (dup) s_dup = 1;
+  }
+  __syncthreads();
+  const bool serial = s_dup != 0;
+  if (serial) {
+    // a token names an expert twice: rank this tile by one thread, in pair order
+    for (int e = tid; e < E; e += kRouteThreads) cnt[e] = 0;
+    __syncthreads();
+    if (tid == 0) {
+      const int64_t t0 = (int64_t)tile * kRouteThreads;
+      const int64_t t1 = t0 + kRouteThreads < a.T ? t0 + kRouteThreads : a.T;
+      for (int64_t p = t0 * k; p < t1 * k; ++p) {
+        const int e = a.ids[p];
+        if (e >= 0 && e < E) a.inv[p] = cnt[e]++;
+      }
+    }
+  } else {
+    for (int e = tid; e < E; e += kRouteThreads) {
+      int run = 0;
+      for (int w = 0; w < kRouteWaves; ++w) {
+        wbase[w * E + e] = run;
+        run += __builtin_popcountll(wmask[w * E + e]);
+      }
+      cnt[e] = run;
+    }
+  }
+  __syncthreads();
+  // rank inside the tile of pair p (expert e) of this thread's token
+  auto rank_of = [&](int64_t p, int e) -> int {
+    return serial ? a.inv[p] : wbase[wv * E + e] + __builtin_popcountll(wmask[wv * E + e] & below);
+  };
+  if (a.ntiles > 1) {
+    for (int e = tid; e < E; e += kRouteThreads) a.tile_counts[(int64_t)tile * E + e] = cnt[e];
+    if (tid == 0) a.tile_counts[(int64_t)a.ntiles * E + tile] = s_bad;
+    if (valid && !serial) {
+      for (int j = 0; j < k; ++j) {
+        const int64_t p = t * k + j;
+        const int e = a.ids[p];
+        if (e >= 0 && e < E) a.inv[p] = rank_of(p, e);
+      }
+    }
+    return;
+  }
+  // one tile: counts, scans, then the scatter
+  for (int e = tid; e < E; e += kRouteThreads) {
+    a.counts[e] = cnt[e];
+    tcnt[e] = a.bm > 0 ? (cnt[e] + a.bm - 1) / a.bm : 0;
+  }
+  __syncthreads();
+  const int total = route_block_scan(cnt, E, tmp);
+  const int ttotal = route_block_scan(tcnt, E, tmp);
+  for (int e = tid; e < E; e += kRouteThreads) {
+    a.offsets[e] = cnt[e];
+    if (a.bm > 0) a.tile_offsets[e] = tcnt[e];
+  }
+  if (tid == 0) {
+    a.offsets[E] = total;
+    if (a.bm > 0) a.tile_offsets[E] = ttotal;
+    a.status[0] = s_bad;
+  }
+  if (valid) {
+    for (int j = 0; j < k; ++j) {
+      const int64_t p = t * k + j;
+      const int e = a.ids[p];
+      if (e < 0 || e >= E) { a.inv[p] = -1; continue; }
+      const int r = cnt[e] + rank_of(p, e);
+      a.sorted[r] = (int)p;
+      a.inv[p] = r;
+    }
+  }
+}
+
+// One item = (token t, run jc of its experts, 32-group grp); consecutive threads take consecutive
+// groups of one token.
+__device__ void route_quantize(const RouteArgs& a, int qb) {
+  const int G = a.H >> 5;
+  const int nj = (a.k + a.kchunk - 1) / a.kchunk;
+  const int64_t items = a.T * nj * G;
+  for (int64_t it = (int64_t)qb * kRouteThreads + threadIdx.x; it < items; it += (int64_t)a.qblocks * kRouteThreads) {
+    const int64_t tj = it / G;
+    const int grp = (int)(it - tj * G);
+    const int64_t t = tj / nj;
+    const int j0 = (int)(tj - t * nj) * a.kchunk;
+    const int j1 = j0 + a.kchunk < a.k ? j0 + a.kchunk : a.k;
+    const u32x4* src = reinterpret_cast<const u32x4*>(a.x + t * a.H + (int64_t)grp * 32);
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x4 w = src[i];
+      const uint32_t b[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        v[8 * i + 2 * h] = __uint_as_float(b[h] << 16);
+        v[8 * i + 2 * h + 1] = __uint_as_float(b[h] & 0xFFFF0000u);
+      }
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
+    for (int j = j0; j < j1; ++j) {
+      const int64_t p = t * a.k + j;
+      const int e = a.ids[p];
+      if (e < 0 || e >= a.E) continue;
+      const float g = a.a_global[e];
+      const int sc = scale_code(amax, g);
+      const float s = e4m3_value(sc);
+      uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < 32; ++i) w[i >> 3] |= nvfp4_code(v[i], s, g) << (4 * (i & 7));
+      *reinterpret_cast<u32x4*>(a.codes + p * (a.H >> 1) + grp * 16) = u32x4{w[0], w[1], w[2], w[3]};
+      a.scales[p * G + grp] = (uint8_t)sc;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  if ((int)blockIdx.x < a.ntiles) route_tile(a, blockIdx.x, smem);
+  else route_quantize(a, blockIdx.x - a.ntiles);
+}
+
+// Several tiles: per expert, the exclusive prefix of the tile counts becomes each (tile, expert)'s
+// global row base; counts, offsets, tile_offsets and status are written.
+__global__ __launch_bounds__(kRouteThreads) void k_route_scan(RouteArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  int* cnt = reinterpret_cast<int*>(smem);      // [E]
+  int* tcnt = cnt + a.E;                        // [E]
+  __shared__ int tmp[kRouteWaves + 1];
+  const int E = a.E, tid = threadIdx.x;
+  for (int e = tid; e < E; e += kRouteThreads) {
+    int run = 0;
+    for (int t = 0; t < a.ntiles; ++t) {
+      const int c = a.tile_counts[(int64_t)t * E + e];
+      a.tile_counts[(int64_t)t * E + e] = run;
+      run += c;
+    }
+    cnt[e] = run;
+    a.counts[e] = run;
+    tcnt[e] = a.bm > 0 ? (run + a.bm - 1) / a.bm : 0;
+  }
+  __syncthreads();
+  const int total = route_block_scan(cnt, E, tmp);
+  const int ttotal = route_block_scan(tcnt, E, tmp);
+  for (int e = tid; e < E; e += kRouteThreads) {
+    a.offsets[e] = cnt[e];
+    if (a.bm > 0) a.tile_offsets[e] = tcnt[e];
+    for (int t = 0; t < a.ntiles; ++t) a.tile_counts[(int64_t)t * E + e] += cnt[e];
+  }
+  if (tid == 0) {
+    a.offsets[E] = total;
+    if (a.bm > 0) a.tile_offsets[E] = ttotal;
+    int bad = 0;
+    for (int t = 0; t < a.ntiles; ++t) bad += a.tile_counts[(int64_t)a.ntiles * E + t];
+    a.status[0] = bad;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_route_scatter(RouteArgs a) {
+  const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (p >= a.T * a.k) return;
+  const int e = a.ids[p];
+  if (e < 0 || e >= a.E) { a.inv[p] = -1; return; }
+  const int64_t tile = (p / a.k) / kRouteThreads;
+  const int r = a.tile_counts[tile * a.E + e] + a.inv[p];
+  a.sorted[r] = (int)p;
+  a.inv[p] = r;
+}
+
+size_t route_scratch_bytes(int64_t T, int E) {
+  const int64_t ntiles = (T + kRouteThreads - 1) / kRouteThreads;
+  return ntiles <= 1 ? 0 : (size_t)ntiles * (E + 1) * 4;
+}
+
+static size_t route_lds_bytes(int E) { return (size_t)kRouteWaves * E * 12 + (size_t)2 * E * 4; }
+
+void launch_route(const int* ids, int64_t T, int k, int E, int* counts, int* offsets, int* tile_offsets, int bm,
+                  int* sorted, int* inv, int* status, void* scratch, const uint16_t* x, int H, const float* a_global,
+                  uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_route), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)route_lds_bytes(1024));
+    attr = true;
+  }
+  RouteArgs a{};
+  a.ids = ids; a.T = T; a.k = k; a.E = E;
+  a.ntiles = T > 0 ? (int)((T + kRouteThreads - 1) / kRouteThreads) : 1;
+  a.counts = counts; a.offsets = offsets; a.tile_offsets = tile_offsets; a.bm = bm;
+  a.sorted = sorted; a.inv = inv; a.status = status;
+  a.tile_counts = static_cast<int*>(scratch);
+  if (x && T > 0) {
+    // enough items to spread a small batch over the chip; a large one encodes all k experts per load
+    const int64_t tg = T * (H >> 5);
+    int64_t nj = (65536 + tg - 1) / tg;
+    nj = nj < 1 ? 1 : (nj > k ? k : nj);
+    a.kchunk = (int)((k + nj - 1) / nj);
+    nj = (k + a.kchunk - 1) / a.kchunk;
+    const int64_t qb = (tg * nj + kRouteThreads - 1) / kRouteThreads;
+    a.qblocks = (int)(qb > 4096 ? 4096 : qb);
+    a.x = x; a.H = H; a.a_global = a_global; a.codes = codes; a.scales = scales;
+  }
+  k_route<<<(unsigned)(a.ntiles + a.qblocks), kRouteThreads, route_lds_bytes(E), stream>>>(a);
+  if (a.ntiles > 1) {
+    k_route_scan<<<1, kRouteThreads, (size_t)2 * E * 4, stream>>>(a);
+    const int64_t P = T * k;
+    k_route_scatter<<<(unsigned)((P + 255) / 256), 256, 0, stream>>>(a);
+  }
+}
+
+// tile_offsets[e] = sum over e' < e of ceil(count_e' / bm), from offsets.
+__global__ __launch_bounds__(kRouteThreads) void k_tile_offsets(const int* offsets, int E, int bm, int* tile_offsets) {
+  __shared__ int c[1024];
+  __shared__ int tmp[kRouteWaves + 1];
+  for (int e = threadIdx.x; e < E; e += kRouteThreads) {
+    const int n = offsets[e + 1] - offsets[e];
+    c[e] = n > 0 ? (n + bm - 1) / bm : 0;
+  }
+  __syncthreads();
+  const int total = route_block_scan(c, E, tmp);
+  for (int e = threadIdx.x; e < E; e += kRouteThreads) tile_offsets[e] = c[e];
+  if (threadIdx.x == 0) tile_offsets[E] = total;
+}
+
+void launch_tile_offsets(const int* offsets, int E, int bm, int* tile_offsets, hipStream_t stream) {
+  k_tile_offsets<<<1, kRouteThreads, 0, stream>>>(offsets, E, bm, tile_offsets);
+}
+
+}  // namespace moesq

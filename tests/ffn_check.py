@@ -48,13 +48,14 @@ def compare_ffn(x, ids, wts, ow13, ow2, g13, g2, gpu_out, gpu, tokens=None, E=No
     xs, ids_s, wts_s = x[tok], ids[tok], wts[tok]
     out_ref, inter = moe.moe_ffn(xs, ids_s, wts_s, ow13, ow2, g13, g2, want=True)
     I = inter["h"].shape[1]
-    # subset sorted row -> GPU row
+    # oracle sorted row of the token subset -> the GPU's pair index (a13 rows) and sorted row (a2 rows)
     p_sub = inter["sorted_pairs"]
     t_sub, j_sub = p_sub // k, p_sub % k
-    gpu_rows = gpu["inv"][tok[t_sub] * k + j_sub]
+    p_full = tok[t_sub] * k + j_sub
+    gpu_rows = gpu["inv"][p_full]
     assert (gpu_rows >= 0).all()
-    assert np.array_equal(gpu["a13_codes"][gpu_rows], inter["a13_codes"]), "gate/up input codes differ"
-    assert np.array_equal(gpu["a13_scales"][gpu_rows], inter["a13_scales"]), "gate/up input scales differ"
+    assert np.array_equal(gpu["a13_codes"][p_full], inter["a13_codes"]), "gate/up input codes differ"
+    assert np.array_equal(gpu["a13_scales"][p_full], inter["a13_scales"]), "gate/up input scales differ"
     a2c_gpu = gpu["a2_codes"][gpu_rows]
     a2s_gpu = gpu["a2_scales"][gpu_rows]
     same = (a2s_gpu == inter["a2_scales"]) & (

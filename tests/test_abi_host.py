@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported():
     for name in decl:
         assert hasattr(L, name), name
     assert sorted(decl) == sorted(moesq.EXPORTED_SYMBOLS)
-    assert moesq.abi_version() == 2
+    assert moesq.abi_version() == 3
 
 
 def test_status_strings():
@@ -66,8 +66,12 @@ def test_argument_checks_return_status_without_launching():
     L.moesq_quantize_act(P, 0, 4, 48, 48, None, None, 0, P, P, P, None)
     assert b"K must be a multiple of 32" in L.moesq_last_error()
     # permute: k out of range, too many experts
-    assert L.moesq_permute(P, 4, 0, 8, P, P, P, P, P, None) == INVALID
-    assert L.moesq_permute(P, 4, 2, 2000, P, P, P, P, P, None) == UNSUPPORTED
+    assert L.moesq_permute(P, 4, 0, 8, P, P, P, P, P, None, 0, None) == INVALID
+    assert L.moesq_permute(P, 4, 2, 2000, P, P, P, P, P, None, 0, None) == UNSUPPORTED
+    # more than one 512-token tile needs scratch
+    assert L.moesq_permute_workspace_size(512, 8) == 0
+    assert L.moesq_permute_workspace_size(513, 8) == 2 * 9 * 4
+    assert L.moesq_permute(P, 1000, 2, 8, P, P, P, P, P, None, 0, None) == WORKSPACE
     # grouped GEMM: K % 256, G, workspace
     w = _weights(K=96)
     assert L.moesq_grouped_gemm(P, P, P, P, 4, ctypes.byref(w), P, P, 1 << 20, None) == UNSUPPORTED

@@ -136,6 +136,27 @@ def test_permute_duplicates_and_invalid_ids():
     assert status.item() == 2
 
 
+def test_permute_one_tile_with_duplicates_among_clean_tiles():
+    # tiles of 512 tokens: only the second holds a token naming an expert twice
+    ids, _ = synth.routing(9, 1500, 64, 6)
+    ids = ids.copy()
+    ids[900, 3] = ids[900, 1]
+    counts, offsets, sorted_, inv, status = moesq.permute(torch.from_numpy(ids).to(DEV), 64)
+    rc, ro, rs, ri = moe.permute(ids, 64)
+    assert np.array_equal(counts.cpu().numpy(), rc)
+    assert np.array_equal(offsets.cpu().numpy(), ro)
+    assert np.array_equal(sorted_.cpu().numpy()[:int(ro[-1])], rs)
+    assert np.array_equal(inv.cpu().numpy(), ri)
+    assert status.item() == 0
+
+
+def test_permute_no_tokens():
+    counts, offsets, sorted_, inv, status = moesq.permute(torch.zeros((0, 4), dtype=torch.int32, device=DEV), 8)
+    assert counts.cpu().numpy().tolist() == [0] * 8
+    assert offsets.cpu().numpy().tolist() == [0] * 9
+    assert status.item() == 0
+
+
 # ------------------------------------------------------------------------------------------------
 # weight compression and storage codec
 # ------------------------------------------------------------------------------------------------
@@ -335,12 +356,11 @@ def test_moe_ffn_full_size_sampled(name, ntok):
     out, inter = _run_ffn(x, ids, wts, w13, w2, g13, g2)
     rc, ro, rs, ri = moe.permute(ids, wl.E)
     assert np.array_equal(inter["offsets"], ro) and np.array_equal(inter["inv"], ri)
-    # every gate/up input row, bit-exact
-    P = int(ro[-1])
+    # every live gate/up input row (pair order: row p = t*k + j), bit-exact
     e_row = ids.ravel()[rs]
     xr = x.float().cpu().numpy()[rs // wl.k]
     rc13, rs13 = nvfp4.quantize(xr, g13[e_row].astype(np.float64))
-    assert np.array_equal(inter["a13_codes"][:P], rc13) and np.array_equal(inter["a13_scales"][:P], rs13)
+    assert np.array_equal(inter["a13_codes"][rs], rc13) and np.array_equal(inter["a13_scales"][rs], rs13)
     toks = np.random.default_rng(1).choice(wl.T, ntok, replace=False)
     touched = sorted(set(ids[toks].ravel().tolist()))
     ow13, ow2 = oracle_layer(dense_expert, touched)
