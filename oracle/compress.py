@@ -6,7 +6,7 @@ scale per 32 K and an FP32 per-tensor global scale) and "Sparse storage layout";
 follows the synthetic recipe (keep the two largest-magnitude pairs, then quantize with
 global = amax/(6*448)) since the trained masks of the pages are not available.
 
-Readings (listed in the design doc): a pair's magnitude is a^2 + b^2, computed in float64 as a*a + b*b
+Readings where the pages are silent: a pair's magnitude is a^2 + b^2, computed in float64 as a*a + b*b
 (no fused multiply-add) from the fp32 values, ties to the lower pair index; the global is the fp32
 quotient fp32(amax of the pruned tensor) / 2688; pruned pairs are the byte 0x00; the kept pairs are
 named by the prune, also where their NVFP4 byte is 0x00.

@@ -6,7 +6,7 @@ paired-4:8 weights, activations quantized per 32 with a global stored per expert
 a paired-4:8 sparse NVFP4 *grouped* GEMM); model cards "Qwen3.8-Flash-Next-P48NVFP4-MoESQ" and
 "Qwen3-30B-A3B-P48NVFP4-MoESQ" (gate and up projections carry separate global scales).
 
-Readings (the design doc lists them): the expert FFN is down(quant(silu(gate) * up)) with
+Readings where the pages are silent: the expert FFN is down(quant(silu(gate) * up)) with
 silu(v) = v / (1 + exp(-v)); gate rows come first in the fused gate|up weight; each expert's gate and
 up outputs take their own weight global; activations are quantized per (token, expert) row with that
 expert's global; the intermediate is kept unrounded before its quantization; each expert's down

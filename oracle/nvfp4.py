@@ -5,7 +5,7 @@ Source: model cards "Qwen3.5-397B-A17B-P48NVFP4-MoESQ" and "Qwen3-30B-A3B-P48NVF
 elements and an FP32 per-tensor global scale; activations are NVFP4 with dynamic per-32 group scales
 and an FP32 global scale stored per expert linear.
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
 
 * value = e2m1(code) * e4m3(scale) * global (the global is multiplicative);
 * scale = E4M3 round-to-nearest-even of the exact real quotient amax / (6 * global), saturating at 448;
