@@ -196,6 +196,9 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run 3 plain device copies of MIB MiB (a known-size kernel for scaling HBM "
+                         "byte counters under rocprofv3 --pmc)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs the expert path on one GPU only; --gpus {args.gpus} is not supported "
@@ -209,6 +212,16 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     ev = HipEvents()
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 3 copies of {n} bytes")
+        del src, dst
     wl = synth.WORKLOADS[args.workload]
     w13, w2, dense_expert = build_layer(wl, args.seed, dev)
     layers = [(w13, w2)]

@@ -80,12 +80,14 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(3)
   uint8_t* sB = smem;                                             // [BMT][RS] f16
   uint16_t* lut_idx = reinterpret_cast<uint16_t*>(smem + BMT * RS);   // [256]
   __shared__ int s_arow[BMT];                                     // activation row of each m-block row
+  __shared__ float s_rw[BMT];                                     // router weight of each row (down)
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int e = blockIdx.x, nb = blockIdx.y;
   const int row0 = p.offsets[e];
   const int M = p.offsets[e + 1] - row0;
   if (M <= 0) return;
+  const EpiScalars es = epi_scalars<EPI>(p, e);
   lut_idx[tid] = (uint16_t)smfmac_index_of_mask_byte((uint32_t)tid);
 
   int wrow[RT];
@@ -98,8 +100,10 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(3)
       const_cast<uint8_t*>(p.a_codes), (short)0, (int)(p.rows * (K >> 1)), kBufferRsrcWord3);
   const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(p.a_scales), (short)0, (int)(p.rows * (K >> 5)), kBufferRsrcWord3);
-  // staging map: thread -> row sn, 32-K groups sq0 .. sq0 + IPT - 1 of each chunk
-  const int sn = tid / kDecTPR, sq0 = (tid % kDecTPR) * IPT;
+  // staging map: thread -> row sn, 32-K groups sq0 .. sq0 + IPT - 1 of each chunk. Consecutive lanes
+  // take consecutive rows, so each LDS write of 8 lanes hits 8 rows at one slot: with the 16 B row
+  // skew that is 8 different bank groups.
+  const int sn = tid % kDecBMT, sq0 = (tid / kDecBMT) * IPT;
 
   for (int m0 = 0; m0 < M; m0 += BMT) {
     const int mrows = M - m0 < BMT ? M - m0 : BMT;
@@ -109,6 +113,7 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(3)
     if (tid < BMT) {
       const int r = row0 + m0 + tid;
       s_arow[tid] = tid < mrows ? (p.a_rows ? p.a_rows[r] : r) : 0;
+      if (EPI == kEpiDown) s_rw[tid] = tid < mrows ? row_weight(p, r) : 0.0f;
     }
     __syncthreads();
     // registers of the activation chunk [k0, k0 + kc): rows past the m-block and groups past the
@@ -198,7 +203,7 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(3)
       for (int d = 0; d < DEPTH - 1; ++d)
         if (gs + d < nsteps) step(d, w[d], -1);
     }
-    if (active) gemm_epilogue<EPI, TG, RT>(p, acc, e, row0, m0, mrows, nb, wv, wrow, lane);
+    if (active) gemm_epilogue<EPI, TG, RT>(p, es, acc, row0, m0, mrows, nb, wv, wrow, s_rw, lane);
   }
 }
 
@@ -217,6 +222,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_prefill(GemmParams p) {
   uint16_t* lut = reinterpret_cast<uint16_t*>(smem + kPreLdsB);
   __shared__ int s_e;
   __shared__ int s_arow[kPreBMT];                 // activation row of each m-block row
+  __shared__ float s_rw[kPreBMT];                 // router weight of each row (down)
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int mb = blockIdx.x, nb = blockIdx.y;
@@ -231,7 +237,9 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_prefill(GemmParams p) {
   if (tid < kPreBMT) {                            // read after the first step's barrier
     const int r = row0 + m0 + tid;
     s_arow[tid] = tid < mrows ? (p.a_rows ? p.a_rows[r] : r) : 0;
+    if (EPI == kEpiDown) s_rw[tid] = tid < mrows ? row_weight(p, r) : 0.0f;
   }
+  const EpiScalars es = epi_scalars<EPI>(p, e);
 
   int wrow[4];
   const bool active = wave_rows<EPI>(p.N, nb, wv, wrow);
@@ -303,7 +311,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_prefill(GemmParams p) {
   }
   if (gs < nsteps) step(gs, wa, wb);
   if (!active) return;
-  gemm_epilogue<EPI, kPreTG>(p, acc, e, row0, m0, mrows, nb, wv, wrow, lane);
+  gemm_epilogue<EPI, kPreTG>(p, es, acc, row0, m0, mrows, nb, wv, wrow, s_rw, lane);
 }
 
 int tactic_rows_per_mblock(int tactic) { return tactic == kTacticPrefill ? kPreBMT : kDecTG * 16; }

@@ -141,21 +141,44 @@ __device__ __forceinline__ int find_expert(const int* tile_offsets, int E, int m
   return *s_e;
 }
 
-// Epilogues. Accumulator acc[rt][tt] of lane (n = lane & 15, q = lane >> 4) holds, for r = 0..3,
-// weight row wrow[rt] + 4q + r and the m-block's token row tt*16 + n.
-template <int EPI, int TG, int RT = 4>
-__device__ __forceinline__ void gemm_epilogue(const GemmParams& p, f32x4 (&acc)[RT][TG], int e, int row0, int m0,
-                                              int mrows, int nb, int wv, const int* wrow, int lane) {
-  const int N = p.N, ntok = lane & 15, qa = lane >> 4;
+// Per-expert scalars of the epilogue, read once at the start of a workgroup (uniform).
+struct EpiScalars {
+  float g0, g1;   // gate/up: activation x weight global of the gate and up halves; store/down: g0 for all rows
+                  // (store with G = 2: g0 first half, g1 second half)
+  float h_global; // gate/up: global of the h quantization
+};
+
+template <int EPI>
+__device__ __forceinline__ EpiScalars epi_scalars(const GemmParams& p, int e) {
+  EpiScalars es;
   const float ag = p.a_global[e];
+  if (EPI == kEpiGateUp || (EPI == kEpiStore && p.G == 2)) {
+    es.g0 = ag * p.w_global[2 * e];
+    es.g1 = ag * p.w_global[2 * e + 1];
+  } else {
+    es.g0 = es.g1 = ag * p.w_global[e];
+  }
+  es.h_global = EPI == kEpiGateUp ? p.h_global[e] : 0.0f;
+  return es;
+}
+
+// Router weight of row r of an m-block (down epilogue), staged in LDS with the m-block's rows.
+__device__ __forceinline__ float row_weight(const GemmParams& p, int row) { return p.topk_weights[p.sorted[row]]; }
+
+// Epilogues. Accumulator acc[rt][tt] of lane (n = lane & 15, q = lane >> 4) holds, for r = 0..3,
+// weight row wrow[rt] + 4q + r and the m-block's token row tt*16 + n. s_rw: router weights of the
+// m-block's rows (down only).
+template <int EPI, int TG, int RT = 4>
+__device__ __forceinline__ void gemm_epilogue(const GemmParams& p, const EpiScalars& es, f32x4 (&acc)[RT][TG],
+                                              int row0, int m0, int mrows, int nb, int wv, const int* wrow,
+                                              const float* s_rw, int lane) {
+  const int N = p.N, ntok = lane & 15, qa = lane >> 4;
   if constexpr (EPI == kEpiGateUp) {
     // h = silu(gate) * up in fp32, then the NVFP4 quantization of h with the down input global:
     // the 32 columns of one scale group are the 8 values of each of the 4 lanes sharing ntok.
     const int I = N >> 1;
     const int hcol0 = nb * 128 + __builtin_amdgcn_readfirstlane(wv) * 32;
-    const float g_gate = ag * p.w_global[2 * e];
-    const float g_up = ag * p.w_global[2 * e + 1];
-    const float g2 = p.h_global[e];
+    const float g2 = es.h_global;
 #pragma unroll
     for (int tt = 0; tt < TG; ++tt) {
       if (tt * 16 >= mrows) continue;
@@ -166,9 +189,10 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, f32x4 (&acc)[
       for (int half = 0; half < 2; ++half)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float gt = acc[half][tt][r] * g_gate;
-          const float up = acc[2 + half][tt][r] * g_up;
-          const float hv = gt / (1.0f + __expf(-gt)) * up;
+          const float gt = acc[half][tt][r] * es.g0;
+          const float up = acc[2 + half][tt][r] * es.g1;
+          // silu(gt) = gt / (1 + exp(-gt)), with the reciprocal instruction (1 ulp)
+          const float hv = gt * up * __builtin_amdgcn_rcpf(1.0f + __expf(-gt));
           h[half][r] = hv;
           amax = __builtin_fmaxf(amax, __builtin_fabsf(hv));
         }
@@ -193,17 +217,15 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, f32x4 (&acc)[
     for (int tt = 0; tt < TG; ++tt) {
       if (tt * 16 >= mrows) continue;
       const int n = tt * 16 + ntok;
-      if (n >= mrows) continue;
-      const int64_t row = row0 + m0 + n;
-      float gsc;
-      if (EPI == kEpiDown) gsc = ag * p.w_global[e] * p.topk_weights[p.sorted[row]];
-      else gsc = ag;
+      if (n < mrows) {
+        const int64_t row = row0 + m0 + n;
+        const float gsc = EPI == kEpiDown ? es.g0 * s_rw[n] : es.g0;
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const int col = wrow[rt] + 4 * qa;
-        float gcol = gsc;
-        if (EPI == kEpiStore) gcol = gsc * (p.G == 2 ? p.w_global[2 * e + (col >= (N >> 1) ? 1 : 0)] : p.w_global[e]);
-        *reinterpret_cast<f32x4*>(p.out + row * N + col) = acc[rt][tt] * gcol;
+        for (int rt = 0; rt < RT; ++rt) {
+          const int col = wrow[rt] + 4 * qa;
+          const float gcol = (EPI == kEpiStore && col >= (N >> 1)) ? es.g1 : gsc;
+          *reinterpret_cast<f32x4*>(p.out + row * N + col) = acc[rt][tt] * gcol;
+        }
       }
     }
   }

@@ -81,6 +81,8 @@ struct RouteArgs {
   int kchunk;                // experts encoded per thread
 };
 
+// KMAX >= k: the token's ids live in registers (static indices), loaded together up front.
+template <int KMAX>
 __device__ void route_tile(const RouteArgs& a, int tile, uint8_t* smem) {
   const int E = a.E, k = a.k;
   unsigned long long* wmask = reinterpret_cast<unsigned long long*>(smem);   // [waves][E]
@@ -94,13 +96,17 @@ __device__ void route_tile(const RouteArgs& a, int tile, uint8_t* smem) {
   const bool valid = t < a.T;
   const unsigned long long bit = 1ull << lane, below = bit - 1ull;
 
+  int ids[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) ids[j] = (valid && j < k) ? a.ids[t * k + j] : -1;
   for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) wmask[i] = 0ull;
   if (tid == 0) { s_bad = 0; s_dup = 0; }
   __syncthreads();
   if (valid) {
     int bad = 0, dup = 0;
-    for (int j = 0; j < k; ++j) {
-      const int e = a.ids[t * k + j];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      const int e = ids[j];
       if (e < 0 || e >= E) { bad += e != -1; continue; }
       const unsigned long long old = atomicOr(&wmask[wv * E + e], bit);
       dup |= (old & bit) != 0ull;
@@ -141,10 +147,11 @@ __device__ void route_tile(const RouteArgs& a, int tile, uint8_t* smem) {
     for (int e = tid; e < E; e += kRouteThreads) a.tile_counts[(int64_t)tile * E + e] = cnt[e];
     if (tid == 0) a.tile_counts[(int64_t)a.ntiles * E + tile] = s_bad;
     if (valid && !serial) {
-      for (int j = 0; j < k; ++j) {
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
         const int64_t p = t * k + j;
-        const int e = a.ids[p];
-        if (e >= 0 && e < E) a.inv[p] = rank_of(p, e);
+        const int e = ids[j];
+        if (j < k && e >= 0 && e < E) a.inv[p] = rank_of(p, e);
       }
     }
     return;
@@ -167,9 +174,11 @@ __device__ void route_tile(const RouteArgs& a, int tile, uint8_t* smem) {
     a.status[0] = s_bad;
   }
   if (valid) {
-    for (int j = 0; j < k; ++j) {
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if (j >= k) continue;
       const int64_t p = t * k + j;
-      const int e = a.ids[p];
+      const int e = ids[j];
       if (e < 0 || e >= E) { a.inv[p] = -1; continue; }
       const int r = cnt[e] + rank_of(p, e);
       a.sorted[r] = (int)p;
@@ -221,9 +230,10 @@ __device__ void route_quantize(const RouteArgs& a, int qb) {
   }
 }
 
+template <int KMAX>
 __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
-  if ((int)blockIdx.x < a.ntiles) route_tile(a, blockIdx.x, smem);
+  if ((int)blockIdx.x < a.ntiles) route_tile<KMAX>(a, blockIdx.x, smem);
   else route_quantize(a, blockIdx.x - a.ntiles);
 }
 
@@ -286,8 +296,9 @@ void launch_route(const int* ids, int64_t T, int k, int E, int* counts, int* off
                   uint8_t* codes, uint8_t* scales, hipStream_t stream) {
   static bool attr = false;
   if (!attr) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_route), hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)route_lds_bytes(1024));
+    for (const void* f : {reinterpret_cast<const void*>(&k_route<8>), reinterpret_cast<const void*>(&k_route<16>),
+                          reinterpret_cast<const void*>(&k_route<32>)})
+      (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)route_lds_bytes(1024));
     attr = true;
   }
   RouteArgs a{};
@@ -307,7 +318,10 @@ void launch_route(const int* ids, int64_t T, int k, int E, int* counts, int* off
     a.qblocks = (int)(qb > 4096 ? 4096 : qb);
     a.x = x; a.H = H; a.a_global = a_global; a.codes = codes; a.scales = scales;
   }
-  k_route<<<(unsigned)(a.ntiles + a.qblocks), kRouteThreads, route_lds_bytes(E), stream>>>(a);
+  const dim3 grid((unsigned)(a.ntiles + a.qblocks));
+  if (k <= 8) k_route<8><<<grid, kRouteThreads, route_lds_bytes(E), stream>>>(a);
+  else if (k <= 16) k_route<16><<<grid, kRouteThreads, route_lds_bytes(E), stream>>>(a);
+  else k_route<32><<<grid, kRouteThreads, route_lds_bytes(E), stream>>>(a);
   if (a.ntiles > 1) {
     k_route_scan<<<1, kRouteThreads, (size_t)2 * E * 4, stream>>>(a);
     const int64_t P = T * k;
