@@ -167,7 +167,10 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(3)
           A[rt] = weight_operand_of<LAYOUT>(frag_word(w.pk[rt], t), s2);
           idx[rt] = lut_idx[(w.mk[rt] >> (8 * t)) & 255u];
         }
-        if (t == 3 && reload >= 0) wp.load(reload, w, active && reload < nsteps);
+        if (t == 3 && reload >= 0) {
+          slot_decoded<RT>(A, idx);
+          wp.load(reload, w, active && reload < nsteps);
+        }
         const int c0 = 8 * (qb >> 1) + 2 * t + (qb & 1);
 #pragma unroll
         for (int tt = 0; tt < TG; ++tt) {
@@ -186,8 +189,12 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(3)
     ActChunk<IPT> ac;
     prefetch(0, K < KC ? K : KC, ac);
     WeightFrag<RT> w[DEPTH];
+    // slot by slot, in order: the loop's waits assume slot d's loads are older than slot d + 1's
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d) wp.load(d, w[d], active && d < nsteps);
+    for (int d = 0; d < DEPTH; ++d) {
+      wp.load(d, w[d], active && d < nsteps);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // One chunk per iteration, its DEPTH super-steps on the DEPTH ring slots.
     int gs = 0;
     for (; gs + DEPTH <= nsteps; gs += DEPTH) {
@@ -204,6 +211,140 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(3)
         if (gs + d < nsteps) step(d, w[d], -1);
     }
     if (active) gemm_epilogue<EPI, TG, RT>(p, es, acc, row0, m0, mrows, nb, wv, wrow, s_rw, lane);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Decode kernel, one staged chunk: K == DEPTH * 256
+// ---------------------------------------------------------------------------------------------
+// A workgroup covers a range of n-blocks of one expert. The m-block's activations (all of K) are
+// staged once and shared by every n-block, instead of once per n-block workgroup, and the weight
+// ring runs on across n-block boundaries: while an n-block computes, the first super-steps of the
+// next one are in flight, so its epilogue also runs under outstanding loads. Loads are issued on
+// every path (past the last n-block as zero-reading out-of-range loads).
+template <int EPI, int LAYOUT, int RT, int DEPTH>
+__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(3))) void k_gemm_decode_nloop(
+    GemmParams p, int nblocks) {
+  constexpr int TG = kDecTG, BMT = kDecBMT;
+  using Geo = DecGeom<DEPTH>;
+  constexpr int RS = Geo::RS, KC = Geo::KC, IPT = Geo::IPT;
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int K = p.K;                                              // == KC
+  uint8_t* sB = smem;                                             // [BMT][RS] f16
+  uint16_t* lut_idx = reinterpret_cast<uint16_t*>(smem + BMT * RS);   // [256]
+  __shared__ int s_arow[BMT];
+  __shared__ float s_rw[BMT];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int e = blockIdx.x;
+  const int nb0 = (int)(((int64_t)blockIdx.y * nblocks) / gridDim.y);
+  const int nb1 = (int)(((int64_t)(blockIdx.y + 1) * nblocks) / gridDim.y);
+  const int row0 = p.offsets[e];
+  const int M = p.offsets[e + 1] - row0;
+  if (M <= 0 || nb0 >= nb1) return;
+  const EpiScalars es = epi_scalars<EPI>(p, e);
+  lut_idx[tid] = (uint16_t)smfmac_index_of_mask_byte((uint32_t)tid);
+  const int nrow = lane & 15, qb = lane >> 4;
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.a_codes), (short)0, (int)(p.rows * (K >> 1)), kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.a_scales), (short)0, (int)(p.rows * (K >> 5)), kBufferRsrcWord3);
+  const int sn = tid % kDecBMT, sq0 = (tid / kDecBMT) * IPT;      // staging map (as k_gemm_decode)
+
+  for (int m0 = 0; m0 < M; m0 += BMT) {
+    const int mrows = M - m0 < BMT ? M - m0 : BMT;
+    const int ntiles = (mrows + 15) >> 4;
+    __syncthreads();
+    if (tid < BMT) {
+      const int r = row0 + m0 + tid;
+      s_arow[tid] = tid < mrows ? (p.a_rows ? p.a_rows[r] : r) : 0;
+      if (EPI == kEpiDown) s_rw[tid] = tid < mrows ? row_weight(p, r) : 0.0f;
+    }
+    __syncthreads();
+    ActChunk<IPT> ac;
+    {
+      const bool srow_live = sn < mrows;
+      const uint32_t ar = (uint32_t)s_arow[srow_live ? sn : 0];
+      const uint32_t cbase = ar * (uint32_t)(K >> 1) + (uint32_t)(sq0 * 16);
+      const uint32_t sbase = ar * (uint32_t)(K >> 5) + (uint32_t)sq0;
+#pragma unroll
+      for (int j = 0; j < IPT; ++j) {
+        ac.v[j] = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, srow_live ? cbase + 16u * j : kOutOfRange, 0, 0);
+        ac.s[j] = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, srow_live ? sbase + j : kOutOfRange, 0, 0);
+      }
+    }
+    int wrow[RT];
+    bool active = wave_rows<EPI, RT>(p.N, nb0, wv, wrow);
+    WeightPtrs<LAYOUT, RT> wp;
+    wp.init(p, e, wrow, active, lane);
+    WeightFrag<RT> w[DEPTH];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      wp.load(d, w[d], active);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // stage the whole K once for all n-blocks of this m-block
+    __syncthreads();
+    if (sn < ntiles * 16) {
+#pragma unroll
+      for (int j = 0; j < IPT; ++j) {
+        const f16 sv = e4m3_to_f16(ac.s[j]);
+        const f16x2 s2 = f16x2{sv, sv};
+        const uint32_t wv4[4] = {ac.v[j].x, ac.v[j].y, ac.v[j].z, ac.v[j].w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+          *reinterpret_cast<u32x4*>(sB + sn * RS + (4 * (sq0 + j) + h) * 16) = act_chunk_kprime(wv4[h], s2);
+      }
+    }
+    __syncthreads();
+    for (int nb = nb0; nb < nb1; ++nb) {
+      int wrow_n[RT];
+      const bool next = nb + 1 < nb1;
+      const bool active_n = wave_rows<EPI, RT>(p.N, next ? nb + 1 : nb, wv, wrow_n) && next;
+      WeightPtrs<LAYOUT, RT> wpn;
+      wpn.init(p, e, wrow_n, active_n, lane);
+      f32x4 acc[RT][TG];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int tt = 0; tt < TG; ++tt) acc[rt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          f16x8 A[RT];
+          int idx[RT];
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            const f16x2 sp = scale_pair_f16(w[d].sc[rt]);
+            const f16x2 s2 = (t < 2) ? __builtin_shufflevector(sp, sp, 0, 0) : __builtin_shufflevector(sp, sp, 1, 1);
+            A[rt] = weight_operand_of<LAYOUT>(frag_word(w[d].pk[rt], t), s2);
+            idx[rt] = lut_idx[(w[d].mk[rt] >> (8 * t)) & 255u];
+          }
+          if (t == 3) {                                             // the next n-block's step d
+            slot_decoded<RT>(A, idx);
+            wpn.load(d, w[d], active_n);
+          }
+          const int c0 = 8 * (qb >> 1) + 2 * t + (qb & 1);
+#pragma unroll
+          for (int tt = 0; tt < TG; ++tt) {
+            if (tt < ntiles) {
+              const uint8_t* bp = sB + (tt * 16 + nrow) * RS + (32 * d + c0) * 16;
+              const u32x4 b0 = *reinterpret_cast<const u32x4*>(bp);
+              const u32x4 b1 = *reinterpret_cast<const u32x4*>(bp + 16 * 16);
+              const f16x16 B = __builtin_bit_cast(f16x16, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+              for (int rt = 0; rt < RT; ++rt)
+                acc[rt][tt] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(A[rt], B, acc[rt][tt], idx[rt], 0, 0);
+            }
+          }
+        }
+      }
+      if (active) gemm_epilogue<EPI, TG, RT>(p, es, acc, row0, m0, mrows, nb, wv, wrow, s_rw, lane);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) wrow[rt] = wrow_n[rt];
+      active = active_n;
+    }
   }
 }
 
@@ -331,14 +472,29 @@ static void set_lds_attr(Kern* k, size_t lds) {
   }
 }
 
+// n-blocks per workgroup of the one-chunk decode kernel: enough to stage the activations once for
+// several n-blocks and to hide each epilogue under the next n-block's loads
+constexpr int kNloopBlocks = 3;
+
 template <int EPI, int LAYOUT>
 static void launch_decode(const GemmParams& p, hipStream_t stream) {
   // gate/up waves own 4 row-tiles (32 columns for the fused quantization); other linears stream
   // 2 row-tiles per wave, which keeps more, shorter streams in flight for short K
   constexpr int RT = EPI == kEpiGateUp ? 4 : 2;
-  const size_t lds = DecGeom<dec_depth(RT)>::lds;
-  set_lds_attr(&k_gemm_decode<EPI, LAYOUT, RT>, lds);
+  constexpr int DEPTH = dec_depth(RT);
   const int nblocks = EPI == kEpiGateUp ? ((p.N >> 1) + 127) / 128 : (p.N + 64 * RT - 1) / (64 * RT);
+  if constexpr (EPI != kEpiGateUp) {
+    if (p.K == DEPTH * 256) {
+      const size_t lds = DecGeom<DEPTH>::lds;
+      set_lds_attr(&k_gemm_decode_nloop<EPI, LAYOUT, RT, DEPTH>, lds);
+      const int ny = (nblocks + kNloopBlocks - 1) / kNloopBlocks;
+      k_gemm_decode_nloop<EPI, LAYOUT, RT, DEPTH>
+          <<<dim3((unsigned)p.E, (unsigned)ny), kGemmThreads, lds, stream>>>(p, nblocks);
+      return;
+    }
+  }
+  const size_t lds = DecGeom<DEPTH>::lds;
+  set_lds_attr(&k_gemm_decode<EPI, LAYOUT, RT>, lds);
   k_gemm_decode<EPI, LAYOUT, RT><<<dim3((unsigned)p.E, (unsigned)nblocks), kGemmThreads, lds, stream>>>(p);
 }
 

@@ -98,6 +98,17 @@ struct WeightPtrs<1, RT> {
   }
 };
 
+// Orders the reload of a weight ring slot after the last decode of its old contents: the (empty)
+// statement consumes the decoded operands and is a memory barrier, so the slot's loads cannot be
+// scheduled above it. Without it the scheduler hoists them, the old and new contents are live at
+// once, and the register allocator rotates the ring through extra registers with copies that wait
+// on loads still in flight.
+template <int RT>
+__device__ __forceinline__ void slot_decoded(const f16x8 (&A)[RT], const int (&idx)[RT]) {
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) asm volatile("" ::"v"(A[rt]), "v"(idx[rt]) : "memory");
+}
+
 // Compressed sparse operand of smfmac t of a fragment word, in either layout.
 template <int LAYOUT>
 __device__ __forceinline__ f16x8 weight_operand_of(uint32_t word, f16x2 s2) {

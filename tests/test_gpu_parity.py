@@ -248,6 +248,9 @@ def test_prepare_layout_and_round_trip():
     (3, 320, 768, 1, [200, 0, 130]),                              # prefill tactic, N not a multiple of 256
     (2, 64, 2048, 2, [1, 129]),
     (5, 128, 1280, 1, [40, 3, 0, 31, 64]),                        # decode, K-chunks of 512 with a short last one
+    (6, 576, 768, 1, [7, 0, 40, 16, 1, 33]),                      # decode, K in one chunk: n-block loop, ragged
+                                                                  # last n-block, several m-blocks
+    (3, 1024, 768, 2, [20, 5, 64]),                               # the same with two global scales
 ])
 def test_grouped_gemm_random_bytes(E, N, K, G, counts, layout):
     packed, mask, scale, gw = synth.random_sparse_weights(12, E, N, K, G)
