@@ -356,14 +356,21 @@ constexpr int kPreBMT = kPreTG * 16;
 constexpr int kPreRowStride = 256 * 2 + 16;   // bytes per token row of one 256-K step in LDS (+16 B skew)
 constexpr int kPreLdsB = kPreBMT * kPreRowStride;
 
+// A workgroup owns one m-block (<= 128 rows of one expert) and 256 weight rows; each wave keeps 4
+// row-tiles x 8 token tiles of accumulators and reuses every decoded weight fragment over the 8
+// token tiles. Per 256-K step the activations are converted to exact f16 in LDS; their codes are
+// prefetched into registers one step ahead (two threads per row, 64 B of codes + 4 scale bytes
+// each), and the weights run through a two-slot register ring reloaded right after decode, so every
+// global load in the K loop is a prefetch issued on every path.
 template <int EPI, int LAYOUT>
 __global__ __launch_bounds__(kGemmThreads) void k_gemm_prefill(GemmParams p) {
+  constexpr int TG = kPreTG, BMT = kPreBMT, RS = kPreRowStride;
   extern __shared__ __align__(16) uint8_t smem[];
-  uint8_t* sB = smem;
+  uint8_t* sB = smem;                              // [BMT][RS] f16 of one 256-K step
   uint16_t* lut = reinterpret_cast<uint16_t*>(smem + kPreLdsB);
   __shared__ int s_e;
-  __shared__ int s_arow[kPreBMT];                 // activation row of each m-block row
-  __shared__ float s_rw[kPreBMT];                 // router weight of each row (down)
+  __shared__ int s_arow[BMT];                      // activation row of each m-block row
+  __shared__ float s_rw[BMT];                      // router weight of each row (down)
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int mb = blockIdx.x, nb = blockIdx.y;
@@ -373,9 +380,10 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_prefill(GemmParams p) {
   if (e < 0) return;
   const int row0 = p.offsets[e];
   const int M = p.offsets[e + 1] - row0;
-  const int m0 = (mb - p.tile_offsets[e]) * kPreBMT;
-  const int mrows = M - m0 < kPreBMT ? M - m0 : kPreBMT;
-  if (tid < kPreBMT) {                            // read after the first step's barrier
+  const int m0 = (mb - p.tile_offsets[e]) * BMT;
+  const int mrows = M - m0 < BMT ? M - m0 : BMT;
+  const int ntiles = (mrows + 15) >> 4;
+  if (tid < BMT) {
     const int r = row0 + m0 + tid;
     s_arow[tid] = tid < mrows ? (p.a_rows ? p.a_rows[r] : r) : 0;
     if (EPI == kEpiDown) s_rw[tid] = tid < mrows ? row_weight(p, r) : 0.0f;
@@ -386,73 +394,102 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_prefill(GemmParams p) {
   const bool active = wave_rows<EPI>(p.N, nb, wv, wrow);
   WeightPtrs<LAYOUT> wp;
   wp.init(p, e, wrow, active, lane);
+  const int nsteps = K >> 8;
+  const int nrow = lane & 15, qb = lane >> 4;
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.a_codes), (short)0, (int)(p.rows * (K >> 1)), kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.a_scales), (short)0, (int)(p.rows * (K >> 5)), kBufferRsrcWord3);
+  // staging map: thread -> row sn, 32-K groups 4 h .. 4 h + 3 of each step; consecutive lanes take
+  // consecutive rows, so each 8-lane LDS write group lands on 8 rows (different banks via the skew)
+  const int sn = tid % BMT, sh = tid / BMT;
+  __syncthreads();                                 // s_arow
+  const bool srow_live = sn < mrows;
+  const uint32_t ar = (uint32_t)s_arow[srow_live ? sn : 0];
+  struct Act { u32x4 v[4]; uint32_t s; };
+  auto prefetch = [&](int gs, Act& ac) {
+    const bool live = srow_live && gs < nsteps;
+    const uint32_t cb = ar * (uint32_t)(K >> 1) + (uint32_t)(gs * 128 + sh * 64);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      ac.v[j] = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, live ? cb + 16u * j : kOutOfRange, 0, 0);
+    ac.s = __builtin_amdgcn_raw_buffer_load_b32(
+        s_rsrc, live ? ar * (uint32_t)(K >> 5) + (uint32_t)(gs * 8 + sh * 4) : kOutOfRange, 0, 0);
+  };
+  auto commit = [&](const Act& ac) {
+    __syncthreads();
+    if (sn < ntiles * 16) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f16x2 sp = scale_pair_f16((ac.s >> (16 * (j >> 1))) & 0xFFFFu);
+        const f16x2 s2 = (j & 1) ? __builtin_shufflevector(sp, sp, 1, 1) : __builtin_shufflevector(sp, sp, 0, 0);
+        const uint32_t wv4[4] = {ac.v[j].x, ac.v[j].y, ac.v[j].z, ac.v[j].w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h)                // 8-K chunk 4 (4 sh + j) + h of the step
+          *reinterpret_cast<u32x4*>(sB + sn * RS + (4 * (4 * sh + j) + h) * 16) = act_chunk_kprime(wv4[h], s2);
+      }
+    }
+    __syncthreads();
+  };
 
-  f32x4 acc[4][kPreTG];
+  f32x4 acc[4][TG];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-    for (int tt = 0; tt < kPreTG; ++tt) acc[rt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int nsteps = K >> 8;
-  WeightFrag<> wa, wb;
-  if (active) wp.load(0, wa);
-  const int64_t a_row_bytes = K >> 1, a_row_scales = K >> 5;
-  // one 256-K step: stage the activations of this K range into LDS, prefetch the next weight
-  // fragment into `nxt`, run the MFMAs on `cur`
-  auto step = [&](int gs, const WeightFrag<>& cur, WeightFrag<>& nxt) {
-    const int k0 = gs * 256;
-    __syncthreads();
-    for (int i = tid; i < kPreBMT * 32; i += kGemmThreads) {
-      const int n = i >> 5, c = i & 31;
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (n < mrows) {
-        const int64_t ar = s_arow[n];
-        const uint32_t codes = *reinterpret_cast<const uint32_t*>(p.a_codes + ar * a_row_bytes + ((k0 >> 3) + c) * 4);
-        const uint32_t sb = p.a_scales[ar * a_row_scales + ((k0 >> 5) + (c >> 2))];
-        const f16 s = e4m3_to_f16(sb);
-        v = act_chunk_kprime(codes, f16x2{s, s});
+    for (int tt = 0; tt < TG; ++tt) acc[rt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto step = [&](WeightFrag<>& w, int reload) {
+    const uint8_t* brow = sB + nrow * RS + (8 * (qb >> 1) + (qb & 1)) * 16;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      f16x8 A[4];
+      int idx[4];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const f16x2 sp = scale_pair_f16(w.sc[rt]);
+        const f16x2 s2 = (t < 2) ? __builtin_shufflevector(sp, sp, 0, 0) : __builtin_shufflevector(sp, sp, 1, 1);
+        A[rt] = weight_operand_of<LAYOUT>(frag_word(w.pk[rt], t), s2);
+        idx[rt] = lut[(w.mk[rt] >> (8 * t)) & 255u];
       }
-      *reinterpret_cast<u32x4*>(sB + n * kPreRowStride + c * 16) = v;
-    }
-    __syncthreads();
-    if (active && gs + 1 < nsteps) wp.load(gs + 1, nxt);
-    if (active) {
-      const int nrow = lane & 15, qb = lane >> 4;
-      const uint8_t* brow = sB + nrow * kPreRowStride + (8 * (qb >> 1) + (qb & 1)) * 16;
+      if (t == 3 && reload >= 0) {
+        slot_decoded<4>(A, idx);
+        wp.load(reload, w, active && reload < nsteps);
+      }
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        f16x8 A[4];
-        int idx[4];
+      for (int tt = 0; tt < TG; ++tt) {
+        if (tt < ntiles) {
+          const uint8_t* bp = brow + tt * 16 * RS + 2 * t * 16;
+          const u32x4 b0 = *reinterpret_cast<const u32x4*>(bp);
+          const u32x4 b1 = *reinterpret_cast<const u32x4*>(bp + 16 * 16);
+          const f16x16 B = __builtin_bit_cast(f16x16, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          const f16x2 sp = scale_pair_f16(cur.sc[rt]);
-          const f16x2 s2 = (t < 2) ? __builtin_shufflevector(sp, sp, 0, 0) : __builtin_shufflevector(sp, sp, 1, 1);
-          A[rt] = weight_operand_of<LAYOUT>(frag_word(cur.pk[rt], t), s2);
-          idx[rt] = lut[(cur.mk[rt] >> (8 * t)) & 255u];
-        }
-#pragma unroll
-        for (int tt = 0; tt < kPreTG; ++tt) {
-          if (tt * 16 < mrows) {
-            const uint8_t* bp = brow + tt * 16 * kPreRowStride + 2 * t * 16;
-            const u32x4 b0 = *reinterpret_cast<const u32x4*>(bp);
-            const u32x4 b1 = *reinterpret_cast<const u32x4*>(bp + 16 * 16);
-            const f16x16 B = __builtin_bit_cast(f16x16, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt)
-              acc[rt][tt] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(A[rt], B, acc[rt][tt], idx[rt], 0, 0);
-          }
+          for (int rt = 0; rt < 4; ++rt)
+            acc[rt][tt] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(A[rt], B, acc[rt][tt], idx[rt], 0, 0);
         }
       }
     }
   };
+  Act ac;
+  prefetch(0, ac);
+  WeightFrag<> w0, w1;
+  wp.load(0, w0, active);
+  __builtin_amdgcn_sched_barrier(0);
+  wp.load(1, w1, active && nsteps > 1);
+  __builtin_amdgcn_sched_barrier(0);
   int gs = 0;
   for (; gs + 2 <= nsteps; gs += 2) {
-    step(gs, wa, wb);
-    step(gs + 1, wb, wa);
+    commit(ac);
+    prefetch(gs + 1, ac);
+    step(w0, gs + 2);
+    commit(ac);
+    prefetch(gs + 2, ac);
+    step(w1, gs + 3);
   }
-  if (gs < nsteps) step(gs, wa, wb);
+  if (gs < nsteps) {                               // odd step count: the last step
+    commit(ac);
+    step(w0, -1);
+  }
   if (!active) return;
-  gemm_epilogue<EPI, kPreTG>(p, es, acc, row0, m0, mrows, nb, wv, wrow, s_rw, lane);
+  gemm_epilogue<EPI, TG>(p, es, acc, row0, m0, mrows, nb, wv, wrow, s_rw, lane);
 }
 
 int tactic_rows_per_mblock(int tactic) { return tactic == kTacticPrefill ? kPreBMT : kDecTG * 16; }
