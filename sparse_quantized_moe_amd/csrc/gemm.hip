@@ -356,6 +356,13 @@ constexpr int kPreBMT = kPreTG * 16;
 constexpr int kPreRowStride = 256 * 2 + 16;   // bytes per token row of one 256-K step in LDS (+16 B skew)
 constexpr int kPreLdsB = kPreBMT * kPreRowStride;
 
+// Work placement: consecutive workgroup ids go to the 8 XCDs in turn, and each XCD has its own L2.
+// Workgroup L therefore takes item (L % 8) * per + L / 8 of the (m-block, n-block) work list, m-block
+// major, where per = ceil(items / 8) for the live item count: each XCD walks a contiguous, balanced
+// range of the list, so the n-blocks of one m-block (same activations) and consecutive m-blocks of
+// one expert (same weights) run side by side on one L2 instead of being fetched by every XCD.
+constexpr int kXcds = 8;
+
 // A workgroup owns one m-block (<= 128 rows of one expert) and 256 weight rows; each wave keeps 4
 // row-tiles x 8 token tiles of accumulators and reuses every decoded weight fragment over the 8
 // token tiles. Per 256-K step the activations are converted to exact f16 in LDS; their codes are
@@ -373,8 +380,14 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_prefill(GemmParams p) {
   __shared__ float s_rw[BMT];                      // router weight of each row (down)
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int mb = blockIdx.x, nb = blockIdx.y;
   const int K = p.K;
+  const int nblocks = EPI == kEpiGateUp ? ((p.N >> 1) + 127) / 128 : (p.N + 255) / 256;
+  const int items = p.tile_offsets[p.E] * nblocks;
+  const int per = (items + kXcds - 1) / kXcds;
+  const int xi = (int)(blockIdx.x / kXcds);
+  const int w_item = (int)(blockIdx.x % kXcds) * per + xi;
+  if (xi >= per || w_item >= items) return;
+  const int mb = w_item / nblocks, nb = w_item - mb * nblocks;
   lut[tid] = (uint16_t)smfmac_index_of_mask_byte((uint32_t)tid);
   const int e = find_expert(p.tile_offsets, p.E, mb, &s_e);
   if (e < 0) return;
@@ -539,9 +552,12 @@ template <int EPI, int LAYOUT>
 static void launch_prefill(const GemmParams& p, hipStream_t stream) {
   const size_t lds = gemm_lds_bytes(kTacticPrefill, p.K);
   set_lds_attr(&k_gemm_prefill<EPI, LAYOUT>, lds);
+  // an upper bound of the live m-blocks (each expert adds at most one partial m-block); the kernel
+  // spreads the live items over the XCDs and the rest of the grid exits
   const int64_t mblocks = (p.rows + kPreBMT - 1) / kPreBMT + p.E;
   const int nblocks = EPI == kEpiGateUp ? ((p.N >> 1) + 127) / 128 : (p.N + 255) / 256;
-  k_gemm_prefill<EPI, LAYOUT><<<dim3((unsigned)mblocks, (unsigned)nblocks), kGemmThreads, lds, stream>>>(p);
+  const int64_t grid = ((mblocks * nblocks + kXcds - 1) / kXcds) * kXcds;
+  k_gemm_prefill<EPI, LAYOUT><<<dim3((unsigned)grid), kGemmThreads, lds, stream>>>(p);
 }
 
 template <int EPI>

@@ -213,11 +213,10 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, const EpiScal
       const float s = e4m3_value(scb);
       if (n < mrows) {
         const int64_t row = row0 + m0 + n;
+        const Nvfp4Recip rc = nvfp4_recip(s, g2);
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          const uint32_t c0 = nvfp4_code(h[half][0], s, g2), c1 = nvfp4_code(h[half][1], s, g2);
-          const uint32_t c2 = nvfp4_code(h[half][2], s, g2), c3 = nvfp4_code(h[half][3], s, g2);
-          const uint16_t v = (uint16_t)(c0 | (c1 << 4) | (c2 << 8) | (c3 << 12));
+          const uint16_t v = (uint16_t)nvfp4_codes<4>(h[half], s, g2, rc);
           *reinterpret_cast<uint16_t*>(p.h_codes + row * (I >> 1) + ((hcol0 + half * 16 + 4 * qa) >> 1)) = v;
         }
         if (qa == 0) p.h_scales[row * (I >> 5) + (hcol0 >> 5)] = (uint8_t)scb;

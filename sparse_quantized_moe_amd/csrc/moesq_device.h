@@ -85,6 +85,52 @@ __device__ __forceinline__ uint32_t nvfp4_code(float x, float s, float g) {
   return e2m1_code(__builtin_fabsf(x), s, g) | ((__float_as_uint(x) >> 28) & 8u);
 }
 
+// Fast exact codes. With sg = s g (one rounding), inv = v_rcp_f32(sg) (at most 1 ulp off) and
+// r = x inv (one rounding), r is within 2^-22 relative of the exact quotient x / (s g), i.e. within
+// 4 ulps of it, as long as sg and inv are normal numbers. The hardware conversion
+// v_cvt_scalef32_pk_fp4_f32 (scale 1) rounds an fp32 value to nearest-even E2M1 with saturation at 6
+// and keeps the sign (checked around every boundary against a host model), so its code equals the
+// exact one unless a rounding boundary lies between r and the exact quotient. Every boundary
+// (0.25 0.75 1.25 1.75 2.5 3.5 5) has at most 2 fraction bits, so that needs r within 4 ulps of such
+// a value; nvfp4_near() flags r within 16 ulps (infinity and NaN included), and a word with a
+// flagged value, or a group whose sg is zero or outside the normal range, takes the exact sign tests.
+struct Nvfp4Recip {
+  float inv;
+  bool exact;  // sg zero, subnormal or too large for a normal reciprocal
+};
+
+__device__ __forceinline__ Nvfp4Recip nvfp4_recip(float s, float g) {
+  const float sg = s * g;
+  return {__builtin_amdgcn_rcpf(sg), !(sg >= 0x1p-126f && sg <= 0x1p125f)};
+}
+
+__device__ __forceinline__ bool nvfp4_near(float r) { return ((__float_as_uint(r) + 16u) & 0x1FFFFFu) < 32u; }
+
+// N (2, 4, 6 or 8) consecutive NVFP4 codes, x[0] in the low nibble, for scale value s and global g;
+// rc = nvfp4_recip(s, g). Equal to the codes of nvfp4_code().
+template <int N>
+__device__ __forceinline__ uint32_t nvfp4_codes(const float* x, float s, float g, Nvfp4Recip rc) {
+  static_assert(N % 2 == 0 && N <= 8, "whole bytes of one word");
+  float r[N];
+  bool near = rc.exact;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    r[i] = x[i] * rc.inv;
+    near = near || nvfp4_near(r[i]);
+  }
+  // the byte selector of the conversion has to be a constant
+  uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, r[0], r[1], 1.0f, 0);
+  if constexpr (N >= 4) w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, r[2], r[3], 1.0f, 1);
+  if constexpr (N >= 6) w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, r[4], r[5], 1.0f, 2);
+  if constexpr (N >= 8) w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, r[6], r[7], 1.0f, 3);
+  if (near) {
+    w = 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) w |= nvfp4_code(x[i], s, g) << (4 * i);
+  }
+  return w;
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
 // ---------------------------------------------------------------------------------------------

@@ -59,10 +59,11 @@ __device__ __forceinline__ uint32_t quantize_group(const float v[32], float g, u
   for (int i = 0; i < 32; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
   const int sc = scale_code(amax, g);
   const float s = e4m3_value(sc);
-  uint32_t w[4] = {0, 0, 0, 0};
-#pragma unroll
-  for (int i = 0; i < 32; ++i) w[i >> 3] |= nvfp4_code(v[i], s, g) << (4 * (i & 7));
-  out.x = w[0]; out.y = w[1]; out.z = w[2]; out.w = w[3];
+  const Nvfp4Recip rc = nvfp4_recip(s, g);
+  out.x = nvfp4_codes<8>(v, s, g, rc);
+  out.y = nvfp4_codes<8>(v + 8, s, g, rc);
+  out.z = nvfp4_codes<8>(v + 16, s, g, rc);
+  out.w = nvfp4_codes<8>(v + 24, s, g, rc);
   return (uint32_t)sc;
 }
 

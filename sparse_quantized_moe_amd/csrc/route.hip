@@ -221,9 +221,10 @@ __device__ void route_quantize(const RouteArgs& a, int qb) {
       const float g = a.a_global[e];
       const int sc = scale_code(amax, g);
       const float s = e4m3_value(sc);
-      uint32_t w[4] = {0, 0, 0, 0};
+      const Nvfp4Recip rc = nvfp4_recip(s, g);
+      uint32_t w[4];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) w[i >> 3] |= nvfp4_code(v[i], s, g) << (4 * (i & 7));
+      for (int h = 0; h < 4; ++h) w[h] = nvfp4_codes<8>(v + 8 * h, s, g, rc);
       *reinterpret_cast<u32x4*>(a.codes + p * (a.H >> 1) + grp * 16) = u32x4{w[0], w[1], w[2], w[3]};
       a.scales[p * G + grp] = (uint8_t)sc;
     }

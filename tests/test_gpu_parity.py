@@ -53,9 +53,12 @@ def test_quantize_bf16_bit_exact(T, H, outliers, gmode):
     assert np.array_equal(codes.cpu().numpy(), rc)
 
 
-def test_quantize_f32_boundaries_bit_exact():
-    """fp32 inputs placed on and next to every E2M1 and E4M3 rounding boundary."""
-    rng = np.random.default_rng(11)
+@pytest.mark.parametrize("spread", [1, 48])
+def test_quantize_f32_boundaries_bit_exact(spread):
+    """fp32 inputs placed on and next to every E2M1 and E4M3 rounding boundary: one ulp either side,
+    or up to `spread` ulps either side (across the window where the kernel switches from the hardware
+    conversion to the exact comparisons)."""
+    rng = np.random.default_rng(11 + spread)
     R = 512
     g = np.float32(0.0371)
     x = np.zeros((R, 64), np.float32)
@@ -65,8 +68,11 @@ def test_quantize_f32_boundaries_bit_exact():
         for gi in range(2):
             # make the group amax give exactly scale s (amax = 6 s g, a +-6 code)
             v = (rng.choice(mids, 32) * s * float(g)).astype(np.float32)
-            v = np.where(rng.random(32) < 0.3, np.nextafter(v, np.float32(np.inf)), v)
-            v = np.where(rng.random(32) < 0.3, np.nextafter(v, np.float32(0)), v)
+            if spread == 1:
+                v = np.where(rng.random(32) < 0.3, np.nextafter(v, np.float32(np.inf)), v)
+                v = np.where(rng.random(32) < 0.3, np.nextafter(v, np.float32(0)), v)
+            else:   # shift the bit pattern by a whole number of ulps (all values are positive here)
+                v = (v.view(np.int32) + rng.integers(-spread, spread + 1, 32).astype(np.int32)).view(np.float32)
             v[0] = np.float32(6 * s * float(g))
             if rng.random() < 0.3:   # amax on an E4M3 midpoint instead
                 i = rng.integers(8, 0x7D)
