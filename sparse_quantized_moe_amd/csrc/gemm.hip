@@ -579,6 +579,9 @@ void launch_grouped_gemm(const GemmParams& p, int epi, int tactic, hipStream_t s
 // ---------------------------------------------------------------------------------------------
 // Top-k combine: out[t] = sum_j D[inv[t*k+j]] in j order (deterministic).
 // ---------------------------------------------------------------------------------------------
+// out[t] = sum over j of D[inv[t k + j]] in order j = 0 .. k-1 (pairs with inv < 0 skipped). The k
+// row indices are loaded first and then all k rows at once.
+template <int KMAX>
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ D, const int* __restrict__ inv,
                                                  int64_t T, int k, int H, float* __restrict__ out) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -586,17 +589,27 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ D, co
   const int64_t t = gid / H4;
   if (t >= T) return;
   const int c = (int)(gid - t * H4) * 4;
+  int r[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) r[j] = j < k ? inv[t * k + j] : -1;
+  f32x4 v[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j)
+    v[j] = r[j] >= 0 ? *reinterpret_cast<const f32x4*>(D + (int64_t)r[j] * H + c) : f32x4{0.f, 0.f, 0.f, 0.f};
   f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) {
-    const int r = inv[t * k + j];
-    if (r >= 0) s += *reinterpret_cast<const f32x4*>(D + (int64_t)r * H + c);
-  }
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j)
+    if (r[j] >= 0) s += v[j];
   *reinterpret_cast<f32x4*>(out + t * H + c) = s;
 }
 
 void launch_combine(const float* D, const int* inv, int64_t T, int k, int H, float* out, hipStream_t stream) {
   const int64_t n = T * (H >> 2);
-  if (n) k_combine<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(D, inv, T, k, H, out);
+  if (!n) return;
+  const unsigned grid = (unsigned)((n + 255) / 256);
+  if (k <= 8) k_combine<8><<<grid, 256, 0, stream>>>(D, inv, T, k, H, out);
+  else if (k <= 16) k_combine<16><<<grid, 256, 0, stream>>>(D, inv, T, k, H, out);
+  else k_combine<32><<<grid, 256, 0, stream>>>(D, inv, T, k, H, out);
 }
 
 }  // namespace moesq

@@ -66,23 +66,33 @@ __device__ __forceinline__ int scale_code(float amax, float g) {
 
 // E2M1 magnitude code (0..7) of the exact quotient ax / (s g): nearest, ties to even, saturating at 6.
 // Boundaries 0.25 .75 1.25 1.75 2.5 3.5 5; a tie goes to the even code (strict '>' where the lower
-// neighbour is even, '>=' where the upper one is). s == 0 gives 0.
+// neighbour is even, '>=' where the upper one is). The code counts the boundaries ax passes, and as
+// they increase it is found by a binary search: 1.75 decides bit 2, then 0.75 or 3.5 bit 1, then
+// 0.25 / 1.25 / 2.5 / 5 bit 0. Each test is the exact sign of ax - B s g: B s is exact (few significant
+// bits) and the FMA rounds once. s == 0 gives 0.
 __device__ __forceinline__ uint32_t e2m1_code(float ax, float s, float g) {
-  if (s == 0.0f) return 0u;
-  uint32_t m = 0;
-  m += __builtin_fmaf(-0.25f * s, g, ax) > 0.0f;
-  m += __builtin_fmaf(-0.75f * s, g, ax) >= 0.0f;
-  m += __builtin_fmaf(-1.25f * s, g, ax) > 0.0f;
-  m += __builtin_fmaf(-1.75f * s, g, ax) >= 0.0f;
-  m += __builtin_fmaf(-2.5f * s, g, ax) > 0.0f;
-  m += __builtin_fmaf(-3.5f * s, g, ax) >= 0.0f;
-  m += __builtin_fmaf(-5.0f * s, g, ax) > 0.0f;
-  return m;
+  const bool h = __builtin_fmaf(-1.75f * s, g, ax) >= 0.0f;
+  const bool m = __builtin_fmaf((h ? -3.5f : -0.75f) * s, g, ax) >= 0.0f;
+  const float b0 = h ? (m ? -5.0f : -2.5f) : (m ? -1.25f : -0.25f);
+  const bool l = __builtin_fmaf(b0 * s, g, ax) > 0.0f;
+  const uint32_t c = (h ? 4u : 0u) | (m ? 2u : 0u) | (l ? 1u : 0u);
+  return s == 0.0f ? 0u : c;
 }
 
 // 4-bit NVFP4 code of x for the group's scale value s and global g (sign bit copied from x).
 __device__ __forceinline__ uint32_t nvfp4_code(float x, float s, float g) {
   return e2m1_code(__builtin_fabsf(x), s, g) | ((__float_as_uint(x) >> 28) & 8u);
+}
+
+// N consecutive NVFP4 codes by the exact comparisons alone, x[0] in the low nibble. For inputs with
+// few significant bits (bf16) many quotients sit within an ulp of a boundary, and the fast path below
+// would take its fallback in nearly every wave.
+template <int N>
+__device__ __forceinline__ uint32_t nvfp4_codes_exact(const float* x, float s, float g) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) w |= nvfp4_code(x[i], s, g) << (4 * i);
+  return w;
 }
 
 // Fast exact codes. With sg = s g (one rounding), inv = v_rcp_f32(sg) (at most 1 ulp off) and
@@ -123,11 +133,7 @@ __device__ __forceinline__ uint32_t nvfp4_codes(const float* x, float s, float g
   if constexpr (N >= 4) w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, r[2], r[3], 1.0f, 1);
   if constexpr (N >= 6) w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, r[4], r[5], 1.0f, 2);
   if constexpr (N >= 8) w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, r[6], r[7], 1.0f, 3);
-  if (near) {
-    w = 0;
-#pragma unroll
-    for (int i = 0; i < N; ++i) w |= nvfp4_code(x[i], s, g) << (4 * i);
-  }
+  if (near) w = nvfp4_codes_exact<N>(x, s, g);
   return w;
 }
 

@@ -52,18 +52,28 @@ __device__ __forceinline__ void load_group(const void* x, int64_t off, float v[3
   }
 }
 
-// Quantize 32 values with global g: writes 16 code bytes and returns the scale byte.
+// Quantize 32 values with global g: writes 16 code bytes and returns the scale byte. fp32 inputs take
+// the hardware conversion with its exact fallback; bf16 inputs (few significant bits, so quotients
+// often sit right on a boundary) take the exact comparisons directly.
+template <bool F32>
 __device__ __forceinline__ uint32_t quantize_group(const float v[32], float g, u32x4& out) {
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
   const int sc = scale_code(amax, g);
   const float s = e4m3_value(sc);
-  const Nvfp4Recip rc = nvfp4_recip(s, g);
-  out.x = nvfp4_codes<8>(v, s, g, rc);
-  out.y = nvfp4_codes<8>(v + 8, s, g, rc);
-  out.z = nvfp4_codes<8>(v + 16, s, g, rc);
-  out.w = nvfp4_codes<8>(v + 24, s, g, rc);
+  if (F32) {
+    const Nvfp4Recip rc = nvfp4_recip(s, g);
+    out.x = nvfp4_codes<8>(v, s, g, rc);
+    out.y = nvfp4_codes<8>(v + 8, s, g, rc);
+    out.z = nvfp4_codes<8>(v + 16, s, g, rc);
+    out.w = nvfp4_codes<8>(v + 24, s, g, rc);
+  } else {
+    out.x = nvfp4_codes_exact<8>(v, s, g);
+    out.y = nvfp4_codes_exact<8>(v + 8, s, g);
+    out.z = nvfp4_codes_exact<8>(v + 16, s, g);
+    out.w = nvfp4_codes_exact<8>(v + 24, s, g);
+  }
   return (uint32_t)sc;
 }
 
@@ -90,7 +100,7 @@ __global__ __launch_bounds__(256) void k_quantize(QuantArgs a) {
   float v[32];
   load_group<F32>(a.x, src * a.stride + (int64_t)grp * 32, v);
   u32x4 out;
-  const uint32_t sc = quantize_group(v, g, out);
+  const uint32_t sc = quantize_group<F32>(v, g, out);
   *reinterpret_cast<u32x4*>(a.codes + r * (a.K >> 1) + grp * 16) = out;
   a.scales[r * G + grp] = (uint8_t)sc;
 }

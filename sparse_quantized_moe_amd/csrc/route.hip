@@ -59,6 +59,47 @@ __device__ int route_block_scan(int* a, int n, int* tmp) {
   return total;
 }
 
+// Exclusive scans in place of a[0..n) and b[0..n) (LDS) in one pass; returns both totals.
+__device__ int2 route_block_scan2(int* a, int* b, int n, int* tmp) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int per = (n + kRouteThreads - 1) / kRouteThreads;
+  const int s0 = tid * per < n ? tid * per : n;
+  const int s1 = s0 + per < n ? s0 + per : n;
+  int sa = 0, sb = 0;
+  for (int i = s0; i < s1; ++i) { sa += a[i]; sb += b[i]; }
+  int va = sa, vb = sb;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int ua = __shfl_up(va, off), ub = __shfl_up(vb, off);
+    if (lane >= off) { va += ua; vb += ub; }
+  }
+  if (lane == 63) { tmp[wv] = va; tmp[kRouteWaves + 1 + wv] = vb; }
+  __syncthreads();
+  if (tid == 0) {
+    int ra = 0, rb = 0;
+    for (int w = 0; w < kRouteWaves; ++w) {
+      const int xa = tmp[w], xb = tmp[kRouteWaves + 1 + w];
+      tmp[w] = ra; tmp[kRouteWaves + 1 + w] = rb;
+      ra += xa; rb += xb;
+    }
+    tmp[kRouteWaves] = ra;
+    tmp[2 * kRouteWaves + 1] = rb;
+  }
+  __syncthreads();
+  int ba = tmp[wv] + va - sa, bb = tmp[kRouteWaves + 1 + wv] + vb - sb;
+  const int2 total = int2{tmp[kRouteWaves], tmp[2 * kRouteWaves + 1]};
+  for (int i = s0; i < s1; ++i) {
+    const int xa = a[i], xb = b[i];
+    a[i] = ba; b[i] = bb;
+    ba += xa; bb += xb;
+  }
+  __syncthreads();
+  return total;
+}
+
+// One tile stages sorted and inv in LDS (written out contiguously afterwards) when they fit.
+constexpr int kRouteStagePairs = 4096;
+
 struct RouteArgs {
   const int* ids;            // [T*k]
   int64_t T;
@@ -89,7 +130,9 @@ __device__ void route_tile(const RouteArgs& a, int tile, uint8_t* smem) {
   int* wbase = reinterpret_cast<int*>(wmask + kRouteWaves * E);              // [waves][E]
   int* cnt = wbase + kRouteWaves * E;                                         // [E]
   int* tcnt = cnt + E;                                                        // [E]
-  __shared__ int tmp[kRouteWaves + 1];
+  int* s_sorted = tcnt + E;                                                   // [T k] (one tile, staged)
+  int* s_inv = s_sorted + kRouteStagePairs;                                   // [T k]
+  __shared__ int tmp[2 * kRouteWaves + 2];
   __shared__ int s_bad, s_dup;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t t = (int64_t)tile * kRouteThreads + tid;
@@ -162,44 +205,62 @@ __device__ void route_tile(const RouteArgs& a, int tile, uint8_t* smem) {
     tcnt[e] = a.bm > 0 ? (cnt[e] + a.bm - 1) / a.bm : 0;
   }
   __syncthreads();
-  const int total = route_block_scan(cnt, E, tmp);
-  const int ttotal = route_block_scan(tcnt, E, tmp);
+  const int2 totals = route_block_scan2(cnt, tcnt, E, tmp);
   for (int e = tid; e < E; e += kRouteThreads) {
     a.offsets[e] = cnt[e];
     if (a.bm > 0) a.tile_offsets[e] = tcnt[e];
   }
   if (tid == 0) {
-    a.offsets[E] = total;
-    if (a.bm > 0) a.tile_offsets[E] = ttotal;
+    a.offsets[E] = totals.x;
+    if (a.bm > 0) a.tile_offsets[E] = totals.y;
     a.status[0] = s_bad;
   }
+  // scatter: through LDS when the pairs fit (scattered LDS writes, then contiguous global writes),
+  // else straight to memory
+  const int64_t P = a.T * k;
+  const bool staged = P <= kRouteStagePairs;
+  int* dst_sorted = staged ? s_sorted : a.sorted;
+  int* dst_inv = staged ? s_inv : a.inv;
   if (valid) {
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
       if (j >= k) continue;
       const int64_t p = t * k + j;
       const int e = ids[j];
-      if (e < 0 || e >= E) { a.inv[p] = -1; continue; }
+      if (e < 0 || e >= E) { dst_inv[p] = -1; continue; }
       const int r = cnt[e] + rank_of(p, e);
-      a.sorted[r] = (int)p;
-      a.inv[p] = r;
+      dst_sorted[r] = (int)p;
+      dst_inv[p] = r;
     }
+  }
+  if (staged) {
+    __syncthreads();
+    for (int i = tid; i < totals.x; i += kRouteThreads) a.sorted[i] = s_sorted[i];
+    for (int i = tid; i < (int)P; i += kRouteThreads) a.inv[i] = s_inv[i];
   }
 }
 
 // One item = (token t, run jc of its experts, 32-group grp); consecutive threads take consecutive
-// groups of one token.
-__device__ void route_quantize(const RouteArgs& a, int qb) {
-  const int G = a.H >> 5;
-  const int nj = (a.k + a.kchunk - 1) / a.kchunk;
-  const int64_t items = a.T * nj * G;
-  for (int64_t it = (int64_t)qb * kRouteThreads + threadIdx.x; it < items; it += (int64_t)a.qblocks * kRouteThreads) {
-    const int64_t tj = it / G;
-    const int grp = (int)(it - tj * G);
-    const int64_t t = tj / nj;
+// groups of one token. The per-expert globals sit in LDS and a run's ids are loaded with the token's
+// values, so an item costs one round trip to memory.
+template <int KMAX>
+__device__ void route_quantize(const RouteArgs& a, int qb, float* s_g) {
+  for (int e = threadIdx.x; e < a.E; e += kRouteThreads) s_g[e] = a.a_global[e];
+  __syncthreads();
+  const uint32_t G = (uint32_t)(a.H >> 5);
+  const uint32_t nj = (uint32_t)((a.k + a.kchunk - 1) / a.kchunk);
+  const uint32_t items = (uint32_t)a.T * nj * G;               // < 2^31 (checked by the host)
+  for (uint32_t it = (uint32_t)qb * kRouteThreads + threadIdx.x; it < items; it += (uint32_t)a.qblocks * kRouteThreads) {
+    const uint32_t tj = it / G;
+    const uint32_t grp = it - tj * G;
+    const uint32_t t = tj / nj;
     const int j0 = (int)(tj - t * nj) * a.kchunk;
-    const int j1 = j0 + a.kchunk < a.k ? j0 + a.kchunk : a.k;
-    const u32x4* src = reinterpret_cast<const u32x4*>(a.x + t * a.H + (int64_t)grp * 32);
+    const int nrun = a.k - j0 < a.kchunk ? a.k - j0 : a.kchunk;
+    const int64_t p0 = (int64_t)t * a.k + j0;
+    int ids[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) ids[j] = j < nrun ? a.ids[p0 + j] : -1;
+    const u32x4* src = reinterpret_cast<const u32x4*>(a.x + (int64_t)t * a.H + grp * 32);
     float v[32];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -214,17 +275,17 @@ __device__ void route_quantize(const RouteArgs& a, int qb) {
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
-    for (int j = j0; j < j1; ++j) {
-      const int64_t p = t * a.k + j;
-      const int e = a.ids[p];
-      if (e < 0 || e >= a.E) continue;
-      const float g = a.a_global[e];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      const int e = ids[j];
+      if (j >= nrun || e < 0 || e >= a.E) continue;
+      const int64_t p = p0 + j;
+      const float g = s_g[e];
       const int sc = scale_code(amax, g);
       const float s = e4m3_value(sc);
-      const Nvfp4Recip rc = nvfp4_recip(s, g);
       uint32_t w[4];
 #pragma unroll
-      for (int h = 0; h < 4; ++h) w[h] = nvfp4_codes<8>(v + 8 * h, s, g, rc);
+      for (int h = 0; h < 4; ++h) w[h] = nvfp4_codes_exact<8>(v + 8 * h, s, g);
       *reinterpret_cast<u32x4*>(a.codes + p * (a.H >> 1) + grp * 16) = u32x4{w[0], w[1], w[2], w[3]};
       a.scales[p * G + grp] = (uint8_t)sc;
     }
@@ -235,7 +296,7 @@ template <int KMAX>
 __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   if ((int)blockIdx.x < a.ntiles) route_tile<KMAX>(a, blockIdx.x, smem);
-  else route_quantize(a, blockIdx.x - a.ntiles);
+  else route_quantize<KMAX>(a, blockIdx.x - a.ntiles, reinterpret_cast<float*>(smem));
 }
 
 // Several tiles: per expert, the exclusive prefix of the tile counts becomes each (tile, expert)'s
@@ -290,7 +351,10 @@ size_t route_scratch_bytes(int64_t T, int E) {
   return ntiles <= 1 ? 0 : (size_t)ntiles * (E + 1) * 4;
 }
 
-static size_t route_lds_bytes(int E) { return (size_t)kRouteWaves * E * 12 + (size_t)2 * E * 4; }
+// masks and bases [waves][E], counts [2][E], then the staged sorted / inv of one tile
+static size_t route_lds_bytes(int E) {
+  return (size_t)kRouteWaves * E * 12 + (size_t)2 * E * 4 + (size_t)2 * kRouteStagePairs * 4;
+}
 
 void launch_route(const int* ids, int64_t T, int k, int E, int* counts, int* offsets, int* tile_offsets, int bm,
                   int* sorted, int* inv, int* status, void* scratch, const uint16_t* x, int H, const float* a_global,
@@ -311,7 +375,7 @@ void launch_route(const int* ids, int64_t T, int k, int E, int* counts, int* off
   if (x && T > 0) {
     // enough items to spread a small batch over the chip; a large one encodes all k experts per load
     const int64_t tg = T * (H >> 5);
-    int64_t nj = (65536 + tg - 1) / tg;
+    int64_t nj = (131072 + tg - 1) / tg;
     nj = nj < 1 ? 1 : (nj > k ? k : nj);
     a.kchunk = (int)((k + nj - 1) / nj);
     nj = (k + a.kchunk - 1) / a.kchunk;
