@@ -11,9 +11,9 @@ top-k combine) over one batch already resident in HBM. The layer's weights (207.
 256 MB Infinity Cache, so decode steps rotate over several copies of the weights (a cold-cache
 stream, the reported value) and the warm single-copy figure is reported beside it.
 
-Output: one JSON line (rank 0). ``roofline`` is for the dominant kernel (the gate/up GEMM), timed with
-HIP events recorded by the library on its own stream; ``cpu_baseline`` times the CPU oracle on a
-bounded sample of the same decode workload.
+Output: one JSON line (rank 0). ``roofline`` is for the dominant kernel (at decode the one-launch
+FFN kernel, else the gate/up GEMM), timed with HIP events recorded by the library on its own stream;
+``cpu_baseline`` times the CPU oracle on a bounded sample of the same decode workload.
 """
 from __future__ import annotations
 
@@ -30,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+DEFAULT_FLAGS = 0              # moe_ffn flags of the timed calls (0: the library's default path)
 F16_DENSE_PEAK_TFLOPS = 2500.0  # MI355X dense f16/bf16 MFMA (the sparse MFMA doubles the dense-equivalent rate)
 
 
@@ -111,7 +112,7 @@ def touched_bytes(ids, E, H, I):
     return n, n * per
 
 
-def run_steps(moesq, torch, ev, x, ids_t, wts_t, layers, g13_t, g2_t, out, ws, warmup, steps, staged=False):
+def run_steps(moesq, torch, ev, x, ids_t, wts_t, layers, g13_t, g2_t, out, ws, warmup, steps, staged=False, flags=0):
     """Untimed warmup, then exactly ``steps`` timed calls bracketed by synchronizations.
 
     Returns (wall seconds, stage times [steps][stages] in ms or None, GPU ms per step). Without
@@ -121,7 +122,7 @@ def run_steps(moesq, torch, ev, x, ids_t, wts_t, layers, g13_t, g2_t, out, ws, w
     ns = len(moesq.FFN_STAGES)
     for i in range(warmup):
         w13, w2 = layers[i % nl]
-        moesq.moe_ffn(x, ids_t, wts_t, w13, w2, g13_t, g2_t, out=out, workspace=ws)
+        moesq.moe_ffn(x, ids_t, wts_t, w13, w2, g13_t, g2_t, out=out, workspace=ws, flags=flags)
     torch.cuda.synchronize()
     evs = [ev.create(ns + 1) for _ in range(steps)] if staged else []
     region = ev.create(2)
@@ -132,7 +133,7 @@ def run_steps(moesq, torch, ev, x, ids_t, wts_t, layers, g13_t, g2_t, out, ws, w
         w13, w2 = layers[i % nl]
         if staged:
             moesq.set_stage_events(evs[i])
-        moesq.moe_ffn(x, ids_t, wts_t, w13, w2, g13_t, g2_t, out=out, workspace=ws)
+        moesq.moe_ffn(x, ids_t, wts_t, w13, w2, g13_t, g2_t, out=out, workspace=ws, flags=flags)
     ev.record(region[1])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -236,33 +237,57 @@ def main():
     out = torch.empty((wl.T, wl.H), dtype=torch.float32, device=dev)
 
     wall, _, gpu_ms = run_steps(moesq, torch, ev, x, ids_t, wts_t, layers, g13_t, g2_t, out, ws,
-                                args.warmup, args.steps)
+                                args.warmup, args.steps, flags=DEFAULT_FLAGS)
     ms = wall / args.steps * 1e3
     n_touched, wbytes = touched_bytes(ids, wl.E, wl.H, wl.I)
     value = wbytes / (wall / args.steps) / 1e9
     log(f"decode: {ms * 1e3:.1f} us/step wall, {gpu_ms * 1e3:.1f} us/step GPU events, {value:.1f} GB/s")
-    # stage breakdown (events between the stages of every call), same rotation of weight copies
+    fused = bool(moesq.ffn_layout(wl.T, wl.H, wl.I, wl.k, wl.E, DEFAULT_FLAGS)["fused"])
+    # stage breakdown (events between the stages of every call), same rotation of weight copies; the
+    # one-launch path records all its stages around its single kernel
     _, stages, st_gpu = run_steps(moesq, torch, ev, x, ids_t, wts_t, layers, g13_t, g2_t, out, ws,
-                                  args.warmup, args.steps, staged=True)
+                                  args.warmup, args.steps, staged=True, flags=DEFAULT_FLAGS)
     st_mean = stages.mean(axis=0)
     log("decode stage us (mean): " + ", ".join(f"{n}={v * 1e3:.1f}" for n, v in zip(moesq.FFN_STAGES, st_mean))
-        + f"; {st_gpu * 1e3:.1f} us/step with stage events")
+        + f"; {st_gpu * 1e3:.1f} us/step with stage events" + (" (one fused launch: all in the first)" if fused else ""))
+    # the other path on the same batch, for comparison (separate launches vs the one-launch kernel)
+    alt = None
+    alt_flags = moesq.FLAG_UNFUSED if fused else moesq.FLAG_FUSED
+    if fused or moesq.ffn_layout(wl.T, wl.H, wl.I, wl.k, wl.E, moesq.FLAG_FUSED)["fused"]:
+        wall_a, _, _ = run_steps(moesq, torch, ev, x, ids_t, wts_t, layers, g13_t, g2_t, out, ws,
+                                 args.warmup, args.steps, flags=alt_flags)
+        _, st_a, _ = run_steps(moesq, torch, ev, x, ids_t, wts_t, layers, g13_t, g2_t, out, ws,
+                               args.warmup, args.steps, staged=True, flags=alt_flags)
+        alt = {"path": "separate launches" if fused else "one fused launch",
+               "us_per_step": round(wall_a / args.steps * 1e6, 2),
+               "GBps": round(wbytes / (wall_a / args.steps) / 1e9, 2),
+               "stage_us": {n: round(float(v) * 1e3, 2) for n, v in zip(moesq.FFN_STAGES, st_a.mean(axis=0))}}
+        log(f"decode, {alt['path']}: {alt['us_per_step']} us/step; stages {alt['stage_us']}")
     # warm (single copy) figure
     wall_w, _, _ = run_steps(moesq, torch, ev, x, ids_t, wts_t, layers[:1], g13_t, g2_t, out, ws,
-                             args.warmup, args.steps)
+                             args.warmup, args.steps, flags=DEFAULT_FLAGS)
     warm = wbytes / (wall_w / args.steps) / 1e9
-    # dominant kernel: gate/up GEMM; algorithmic bytes = W13 stored bytes of touched experts + its
-    # activation input (codes + scales) + its output (down-input codes + scales)
     P = int((ids >= 0).sum())
-    w13_bytes = n_touched * (2 * wl.I * wl.H * 11 // 32 + 8)
-    gemm_bytes = w13_bytes + P * (wl.H // 2 + wl.H // 32) + P * (wl.I // 2 + wl.I // 32)
-    gemm_ms = float(st_mean[moesq.FFN_STAGES.index("gemm_gate_up")])
-    achieved = gemm_bytes / (gemm_ms * 1e-3) / 1e9
+    if fused:
+        # dominant (only) kernel: the fused FFN; algorithmic bytes = stored weight bytes of the touched
+        # experts + the tokens in (bf16) + router ids and weights + the output (fp32)
+        kname = "k_ffn_fused (route, gate/up, down, combine in one launch)"
+        kbytes = wbytes + wl.T * wl.H * 2 + P * 8 + wl.T * wl.H * 4
+        k_ms = float(st_mean.sum())
+        tname, tsrc = "traffic_ffn_fused_qwen3_30b_decode.json", ("ffn_fused.hip", "gemm_common.h", "moesq_device.h")
+    else:
+        # dominant kernel: gate/up GEMM; algorithmic bytes = W13 stored bytes of touched experts + its
+        # activation input (codes + scales) + its output (down-input codes + scales)
+        kname = "k_gemm_decode_stream<gate_up>"
+        kbytes = n_touched * (2 * wl.I * wl.H * 11 // 32 + 8) + P * (wl.H // 2 + wl.H // 32) + P * (wl.I // 2 + wl.I // 32)
+        k_ms = float(st_mean[moesq.FFN_STAGES.index("gemm_gate_up")])
+        tname, tsrc = "traffic_gemm_gate_up_qwen3_30b_decode.json", ("gemm.hip", "gemm_common.h", "moesq_device.h")
+    achieved = kbytes / (k_ms * 1e-3) / 1e9
     traffic = None
-    tfile = os.path.join(ROOT, "profiles", "traffic_gemm_gate_up_qwen3_30b_decode.json")
+    tfile = os.path.join(ROOT, "profiles", tname)
     if os.path.exists(tfile):
         t = json.load(open(tfile))
-        if t.get("kernel_source_sha") == _kernel_sha():
+        if t.get("kernel_source_sha") == _kernel_sha(tsrc):
             traffic = t.get("bytes_per_launch")
     result = {
         "metric": "MoE FFN effective dense TFLOP/s (prefill) + weight-stream GB/s (decode), 1 GPU",
@@ -272,12 +297,13 @@ def main():
         "config": {"workload": wl.name, "experts": wl.E, "top_k": wl.k, "hidden": wl.H, "moe_intermediate": wl.I,
                    "tokens": wl.T, "experts_touched": n_touched, "stored_bytes_streamed": wbytes,
                    "weight_copies_rotated": args.copies, "warm_cache_GBps": round(warm, 2),
-                   "gpu_us_per_step": round(gpu_ms * 1e3, 2),
-                   "stage_us": {n: round(float(v) * 1e3, 2) for n, v in zip(moesq.FFN_STAGES, st_mean)}},
-        "roofline": {"bound": "hbm", "kernel": "k_grouped_gemm<gate_up> (decode tactic)", "achieved": round(achieved, 2),
+                   "gpu_us_per_step": round(gpu_ms * 1e3, 2), "fused_launch": fused,
+                   "stage_us": {n: round(float(v) * 1e3, 2) for n, v in zip(moesq.FFN_STAGES, st_mean)},
+                   "other_path": alt},
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "algorithmic_bytes_per_launch": gemm_bytes,
-                     "avg_launch_us": round(gemm_ms * 1e3, 2)},
+                     "traffic": traffic, "algorithmic_bytes_per_launch": kbytes,
+                     "avg_launch_us": round(k_ms * 1e3, 2)},
     }
     del layers[1:]
     torch.cuda.empty_cache()
@@ -320,10 +346,10 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def _kernel_sha() -> str:
+def _kernel_sha(files) -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in ("gemm.hip", "moesq_device.h"):
+    for f in files:
         h.update(open(os.path.join(ROOT, "sparse_quantized_moe_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 

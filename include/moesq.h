@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define MOESQ_ABI_VERSION 3
+#define MOESQ_ABI_VERSION 4
 /* quantization_config marker "paired48_sparse": {"layout": "pair-bitmask", "version": 1} */
 #define MOESQ_PAIR_BITMASK_VERSION 1
 
@@ -53,6 +53,8 @@ typedef enum { MOESQ_BF16 = 0, MOESQ_F32 = 1 } moesq_dtype;
 
 /* moe_ffn flags */
 #define MOESQ_FLAG_SYNC_CHECK 1u    /* synchronize the stream before returning and report kernel errors */
+#define MOESQ_FLAG_UNFUSED 2u       /* moe_ffn: separate launches even where the one-launch path applies */
+#define MOESQ_FLAG_FUSED 4u         /* moe_ffn: the one-launch decode path wherever it applies */
 
 /* Weight layouts.
  * MOESQ_LAYOUT_PAIR_BITMASK: the stored tensors packed / mask / scale as above, per expert.
@@ -139,12 +141,18 @@ moesq_status moesq_grouped_gemm(const uint8_t *a_codes, const uint8_t *a_scales,
  *   moesq_permute writes them), the gate/up input codes+scales a13 in pair order (row p = t*k + j,
  *   rows of dropped pairs unwritten), the down input codes+scales a2 and the per-row down outputs
  *   (already times the router weight) in sorted order (row inv[p]); route_scratch is the
- *   permutation's scratch. */
+ *   permutation's scratch.
+ *   Decode sizes (tiled weights, H and I <= 2048, T*k <= 4096, mean rows per expert <= 48, and one
+ *   workgroup per (expert, 384 columns of I) resident at once) can run as one cooperative launch
+ *   (MOESQ_FLAG_FUSED; layout.fused = 1): same results and intermediates, except that tile_offsets and route_scratch
+ *   are not written; `sync` is its barrier area (any initial contents). If a barrier wait of
+ *   that launch runs out (it should not), status[0] reads -1 and the outputs are not valid. */
 typedef struct {
   size_t counts, offsets, tile_offsets, sorted, inv, status;
-  size_t a13_codes, a13_scales, a2_codes, a2_scales, down_rows, route_scratch;
+  size_t a13_codes, a13_scales, a2_codes, a2_scales, down_rows, route_scratch, sync;
   size_t total;
   int32_t rows_per_mblock;   /* m-block size of the tactic the call uses */
+  int32_t fused;             /* 1: a call with tiled weights runs as one cooperative launch */
 } moesq_ffn_layout;
 moesq_status moesq_moe_ffn_layout(int64_t T, int32_t H, int32_t I, int32_t k, int32_t E, uint32_t flags,
                                   moesq_ffn_layout *layout /* host */);

@@ -20,12 +20,14 @@ import torch
 __all__ = [
     "MoesqError", "SparseWeights", "lib", "library_path", "abi_version", "quantize_act", "permute",
     "grouped_gemm", "moe_ffn", "ffn_layout", "compress_weights", "compress_moe_layer", "validate_weights",
-    "pack_pair_bitmask", "unpack_pair_bitmask", "FLAG_SYNC_CHECK", "EXPORTED_SYMBOLS",
+    "pack_pair_bitmask", "unpack_pair_bitmask", "FLAG_SYNC_CHECK", "FLAG_UNFUSED", "FLAG_FUSED", "EXPORTED_SYMBOLS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_PKG, "libmoesq.so")
 FLAG_SYNC_CHECK = 1
+FLAG_UNFUSED = 2      # moe_ffn: separate launches even where the one-launch decode path applies
+FLAG_FUSED = 4        # moe_ffn: the one-launch decode path wherever it applies
 
 #: Every function the C ABI exports (include/moesq.h).
 EXPORTED_SYMBOLS = (
@@ -54,7 +56,8 @@ LAYOUT_TILED = 1
 class _CLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in ("counts", "offsets", "tile_offsets", "sorted", "inv", "status",
                                                 "a13_codes", "a13_scales", "a2_codes", "a2_scales",
-                                                "down_rows", "route_scratch", "total")] + [("rows_per_mblock", ctypes.c_int32)]
+                                                "down_rows", "route_scratch", "sync", "total")] + \
+        [("rows_per_mblock", ctypes.c_int32), ("fused", ctypes.c_int32)]
 
 
 _lib: Optional[ctypes.CDLL] = None

@@ -60,6 +60,13 @@ int ffn_tactic(int64_t rows, int32_t E, int32_t K1, int32_t K2) {
   return (rows <= (int64_t)48 * E && fits) ? moesq::kTacticDecode : moesq::kTacticPrefill;
 }
 
+// The one-launch decode path (ffn_fused.hip) for the decode tactic when the shapes and the device
+// allow it and the caller asks for it.
+bool ffn_fused(int64_t T, int32_t H, int32_t I, int32_t k, int32_t E, int tactic, uint32_t flags) {
+  const bool want = (flags & MOESQ_FLAG_FUSED) && !(flags & MOESQ_FLAG_UNFUSED);
+  return want && tactic == moesq::kTacticDecode && moesq::fused_applicable(T, H, I, k, E);
+}
+
 }  // namespace
 
 extern "C" {
@@ -154,7 +161,6 @@ moesq_status moesq_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
 
 moesq_status moesq_moe_ffn_layout(int64_t T, int32_t H, int32_t I, int32_t k, int32_t E, uint32_t flags,
                                   moesq_ffn_layout* L) {
-  (void)flags;
   MOESQ_REQUIRE(L, MOESQ_ERR_INVALID, "moe_ffn_layout: null layout");
   MOESQ_REQUIRE(T >= 0 && H > 0 && I > 0 && k >= 1 && E >= 1, MOESQ_ERR_INVALID, "moe_ffn_layout: bad sizes");
   const size_t P = (size_t)T * k;
@@ -172,8 +178,11 @@ moesq_status moesq_moe_ffn_layout(int64_t T, int32_t H, int32_t I, int32_t k, in
   L->a2_scales = take(P * (size_t)(I / 32));
   L->down_rows = take(P * (size_t)H * 4);
   L->route_scratch = take(moesq::route_scratch_bytes(T, E));
+  L->sync = take(moesq::kFusedSyncBytes);
   L->total = off;
-  L->rows_per_mblock = moesq::tactic_rows_per_mblock(ffn_tactic(T * k, E, H, I));
+  const int tactic = ffn_tactic(T * k, E, H, I);
+  L->rows_per_mblock = moesq::tactic_rows_per_mblock(tactic);
+  L->fused = ffn_fused(T, H, I, k, E, tactic, flags) ? 1 : 0;
   return MOESQ_OK;
 }
 
@@ -223,6 +232,21 @@ moesq_status moesq_moe_ffn(const void* x, int64_t T, int32_t H, const int32_t* t
   float* drows = reinterpret_cast<float*>(ws + L.down_rows);
   const int tactic = ffn_tactic(T * k, E, H, I);
   const int64_t P = T * k;
+
+  if (L.fused && w13->layout == 1 && w2->layout == 1) {
+    moesq::FusedLaunch f{};
+    f.x = static_cast<const uint16_t*>(x); f.ids = topk_ids; f.topk_weights = topk_weights;
+    f.a13_global = a13_global; f.a2_global = a2_global;
+    f.w13 = w13->packed; f.w13_global = w13->global; f.w2 = w2->packed; f.w2_global = w2->global;
+    f.T = T; f.H = H; f.I = I; f.k = k; f.E = E;
+    f.counts = counts; f.offsets = offsets; f.sorted = sorted; f.inv = inv; f.status = status;
+    f.a13c = a13c; f.a13s = a13s; f.a2c = a2c; f.a2s = a2s; f.D = drows; f.out = out; f.sync = ws + L.sync;
+    stage_event(0, stream);
+    const hipError_t err = moesq::launch_ffn_fused(f, stream);
+    for (int i = 1; i <= 4; ++i) stage_event(i, stream);
+    if (err != hipSuccess) return fail(MOESQ_ERR_HIP, "moe_ffn: fused launch: %s", hipGetErrorString(err));
+    return check_launch(stream, (flags & MOESQ_FLAG_SYNC_CHECK) != 0);
+  }
 
   // routing: permutation + gate/up input quantization (pair order)
   stage_event(0, stream);

@@ -349,6 +349,147 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(3)
 }
 
 // ---------------------------------------------------------------------------------------------
+// Decode kernel, whole K staged (tiled weights, K <= kStreamMaxK)
+// ---------------------------------------------------------------------------------------------
+// One workgroup of kStreamWaves waves per (expert, column group): at the decode shapes the grid is
+// one workgroup per CU, and the m-block's activations, all of K as exact f16 (32 rows x 2K bytes),
+// are staged in LDS once and read by every wave. The weight ring's first loads go out before the
+// staging, and the K loop has no barrier: each wave streams its own row-tiles through its register
+// ring and runs its epilogue as soon as it is done, so the waves of a CU keep the loads in flight
+// that one short-lived workgroup per n-block could not.
+constexpr int kStreamWaves = 12;
+constexpr int kStreamThreads = kStreamWaves * 64;
+constexpr int kStreamMaxK = 2048;
+constexpr int kStreamItems = (kDecBMT * (kStreamMaxK / 32) + kStreamThreads - 1) / kStreamThreads;  // staging items per thread
+
+__host__ __device__ constexpr size_t stream_lds_bytes(int K) { return (size_t)kDecBMT * (K * 2 + 16) + 512; }
+
+template <int EPI, int RT, int DEPTH>
+__global__ __launch_bounds__(kStreamThreads) __attribute__((amdgpu_waves_per_eu(3))) void k_gemm_decode_stream(GemmParams p) {
+  constexpr int TG = kDecTG, BMT = kDecBMT;
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int K = p.K, RS = K * 2 + 16;
+  uint8_t* sB = smem;                                                     // [BMT][RS] f16
+  uint16_t* lut_idx = reinterpret_cast<uint16_t*>(smem + BMT * RS);       // [256]
+  __shared__ int s_arow[BMT];
+  __shared__ float s_rw[BMT];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int e = blockIdx.x;
+  const int gw = (int)blockIdx.y * kStreamWaves + wv;                    // wave index in the expert
+  const int row0 = p.offsets[e];
+  const int M = p.offsets[e + 1] - row0;
+  if (M <= 0) return;
+  const EpiScalars es = epi_scalars<EPI>(p, e);
+  if (tid < 256) lut_idx[tid] = (uint16_t)smfmac_index_of_mask_byte((uint32_t)tid);
+  int wrow[RT];
+  const bool active = wave_rows<EPI, RT>(p.N, 0, gw, wrow);
+  WeightPtrs<1, RT> wp;
+  wp.init(p, e, wrow, active, lane);
+  const int nsteps = K >> 8, G = K >> 5;
+  const int nrow = lane & 15, qb = lane >> 4;
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.a_codes), (short)0, (int)(p.rows * (K >> 1)), kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.a_scales), (short)0, (int)(p.rows * (K >> 5)), kBufferRsrcWord3);
+
+  for (int m0 = 0; m0 < M; m0 += BMT) {
+    const int mrows = M - m0 < BMT ? M - m0 : BMT;
+    const int ntiles = (mrows + 15) >> 4;
+    // the m-block's weight stream starts before its activations are staged
+    WeightFrag<RT> w[DEPTH];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      wp.load(d, w[d], active && d < nsteps);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();                        // every wave is done with the previous m-block's LDS
+    if (tid < BMT) {
+      const int r = row0 + m0 + tid;
+      s_arow[tid] = tid < mrows ? (p.a_rows ? p.a_rows[r] : r) : 0;
+      if (EPI == kEpiDown) s_rw[tid] = tid < mrows ? row_weight(p, r) : 0.0f;
+    }
+    __syncthreads();
+    // staging: item i = (32-K group q, row n), rows fastest so that the 8 lanes of an LDS write group
+    // hit 8 rows; every load is issued before the first is used, rows past the m-block read zeros
+    {
+      u32x4 cv[kStreamItems];
+      uint32_t sv[kStreamItems];
+#pragma unroll
+      for (int j = 0; j < kStreamItems; ++j) {
+        const int i = tid + j * kStreamThreads;
+        const int n = i % BMT, q = i / BMT;
+        const bool live = n < mrows && q < G;
+        const uint32_t ar = (uint32_t)s_arow[n];
+        cv[j] = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, live ? ar * (uint32_t)(K >> 1) + 16u * q : kOutOfRange, 0, 0);
+        sv[j] = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, live ? ar * (uint32_t)G + q : kOutOfRange, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < kStreamItems; ++j) {
+        const int i = tid + j * kStreamThreads;
+        const int n = i % BMT, q = i / BMT;
+        if (n < ntiles * 16 && q < G) {
+          const f16 svh = e4m3_to_f16(sv[j]);
+          const f16x2 s2 = f16x2{svh, svh};
+          const uint32_t wv4[4] = {cv[j].x, cv[j].y, cv[j].z, cv[j].w};
+#pragma unroll
+          for (int h = 0; h < 4; ++h)
+            *reinterpret_cast<u32x4*>(sB + n * RS + (4 * q + h) * 16) = act_chunk_kprime(wv4[h], s2);
+        }
+      }
+    }
+    __syncthreads();
+    f32x4 acc[RT][TG];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int tt = 0; tt < TG; ++tt) acc[rt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // super-step gs on weight fragment w; once its last word is decoded, w is reloaded with
+    // super-step `reload` (< 0: none)
+    auto step = [&](int gs, WeightFrag<RT>& w, int reload) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        f16x8 A[RT];
+        int idx[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const f16x2 sp = scale_pair_f16(w.sc[rt]);
+          const f16x2 s2 = (t < 2) ? __builtin_shufflevector(sp, sp, 0, 0) : __builtin_shufflevector(sp, sp, 1, 1);
+          A[rt] = weight_operand_tiled(frag_word(w.pk[rt], t), s2);
+          idx[rt] = lut_idx[(w.mk[rt] >> (8 * t)) & 255u];
+        }
+        if (t == 3 && reload >= 0) {
+          slot_decoded<RT>(A, idx);
+          wp.load(reload, w, active && reload < nsteps);
+        }
+        const int c0 = 8 * (qb >> 1) + 2 * t + (qb & 1);
+#pragma unroll
+        for (int tt = 0; tt < TG; ++tt) {
+          if (tt < ntiles) {
+            const uint8_t* bp = sB + (tt * 16 + nrow) * RS + (32 * gs + c0) * 16;
+            const u32x4 b0 = *reinterpret_cast<const u32x4*>(bp);
+            const u32x4 b1 = *reinterpret_cast<const u32x4*>(bp + 16 * 16);
+            const f16x16 B = __builtin_bit_cast(f16x16, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+              acc[rt][tt] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(A[rt], B, acc[rt][tt], idx[rt], 0, 0);
+          }
+        }
+      }
+    };
+    int gs = 0;
+    for (; gs + DEPTH <= nsteps; gs += DEPTH) {
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) step(gs + d, w[d], gs + DEPTH + d);
+    }
+#pragma unroll
+    for (int d = 0; d < DEPTH - 1; ++d)
+      if (gs + d < nsteps) step(gs + d, w[d], -1);
+    if (active) gemm_epilogue<EPI, TG, RT>(p, es, acc, row0, m0, mrows, 0, gw, wrow, s_rw, lane);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // Prefill kernel
 // ---------------------------------------------------------------------------------------------
 constexpr int kPreTG = 8;
@@ -532,6 +673,16 @@ static void launch_decode(const GemmParams& p, hipStream_t stream) {
   // 2 row-tiles per wave, which keeps more, shorter streams in flight for short K
   constexpr int RT = EPI == kEpiGateUp ? 4 : 2;
   constexpr int DEPTH = dec_depth(RT);
+  if constexpr (EPI == kEpiGateUp && LAYOUT == 1) {
+    if (p.K <= kStreamMaxK) {
+      const size_t lds = stream_lds_bytes(p.K);
+      set_lds_attr(&k_gemm_decode_stream<EPI, RT, DEPTH>, stream_lds_bytes(kStreamMaxK));
+      const int waves = (p.N >> 1) / 32;
+      const int groups = (waves + kStreamWaves - 1) / kStreamWaves;
+      k_gemm_decode_stream<EPI, RT, DEPTH><<<dim3((unsigned)p.E, (unsigned)groups), kStreamThreads, lds, stream>>>(p);
+      return;
+    }
+  }
   const int nblocks = EPI == kEpiGateUp ? ((p.N >> 1) + 127) / 128 : (p.N + 64 * RT - 1) / (64 * RT);
   if constexpr (EPI != kEpiGateUp) {
     if (p.K == DEPTH * 256) {

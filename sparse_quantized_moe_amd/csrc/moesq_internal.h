@@ -75,6 +75,37 @@ struct GemmParams {
 };
 void launch_grouped_gemm(const GemmParams& p, int epi, int tactic, hipStream_t stream);
 
+// Decode-size FFN in one cooperative launch (ffn_fused.hip): tiled weights, H, I <= 2048,
+// T*k <= 4096, and every (expert, part) workgroup resident at once.
+struct FusedLaunch {
+  const uint16_t* x;
+  const int* ids;
+  const float* topk_weights;
+  const float* a13_global;
+  const float* a2_global;
+  const uint8_t* w13;
+  const float* w13_global;
+  const uint8_t* w2;
+  const float* w2_global;
+  int64_t T;
+  int H, I, k, E;
+  int* counts;
+  int* offsets;
+  int* sorted;
+  int* inv;
+  int* status;
+  uint8_t* a13c;
+  uint8_t* a13s;
+  uint8_t* a2c;
+  uint8_t* a2s;
+  float* D;
+  float* out;
+  uint8_t* sync;      // kFusedSyncBytes of workspace: release word, error word, arrival flags (any contents)
+};
+constexpr size_t kFusedSyncBytes = 64 + 8 * 1024;
+bool fused_applicable(int64_t T, int H, int I, int k, int E);
+hipError_t launch_ffn_fused(const FusedLaunch& f, hipStream_t stream);
+
 // out[t][:] = sum_j D[inv[t*k + j]][:] (rows with inv < 0 skipped), in j order.
 void launch_combine(const float* D, const int* inv, int64_t T, int k, int H, float* out, hipStream_t stream);
 

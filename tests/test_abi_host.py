@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported():
     for name in decl:
         assert hasattr(L, name), name
     assert sorted(decl) == sorted(moesq.EXPORTED_SYMBOLS)
-    assert moesq.abi_version() == 3
+    assert moesq.abi_version() == 4
 
 
 def test_status_strings():

@@ -375,3 +375,63 @@ def test_moe_ffn_full_size_sampled(name, ntok):
     ow13, ow2 = oracle_layer(dense_expert, touched)
     st = compare_ffn(x.float().cpu().numpy(), ids, wts, ow13, ow2, g13, g2, out, inter, tokens=toks)
     print(name, st)
+
+
+def _ffn_both_paths(x, ids, wts, w13, w2, g13, g2):
+    """moe_ffn on the one-launch path and on the separate launches (same inputs, own workspaces)."""
+    T, H = x.shape
+    k = ids.shape[1]
+    E, I = w13.E, w2.K
+    res = []
+    for flags in (moesq.FLAG_FUSED, moesq.FLAG_UNFUSED):
+        lay = moesq.ffn_layout(T, H, I, k, E, flags)
+        ws = torch.empty(lay["total"], dtype=torch.uint8, device=DEV)
+        ws.fill_(0xA5)                                   # arbitrary contents, barrier area included
+        out = moesq.moe_ffn(x, torch.from_numpy(ids).to(DEV), torch.from_numpy(wts).to(DEV), w13, w2,
+                            torch.from_numpy(g13).to(DEV), torch.from_numpy(g2).to(DEV), workspace=ws, flags=flags)
+        inter = {kk: v.cpu().numpy() for kk, v in moesq.ffn_intermediates(ws, T, H, I, k, E).items()}
+        res.append((lay["fused"], out.cpu().numpy(), inter))
+    return res
+
+
+@pytest.mark.parametrize("case", ["qwen3_30b_decode", "dup_invalid", "skewed"])
+def test_moe_ffn_fused_matches_separate_launches(case):
+    """The one-launch decode path against the separate launches, bit for bit: output and every
+    intermediate (rows of dropped pairs excepted). Duplicate and invalid router ids, and an expert with
+    more than one m-block (32 rows), are covered by the small cases."""
+    if case == "qwen3_30b_decode":
+        wl = synth.WORKLOADS[case]
+        E, H, I, T, k = wl.E, wl.H, wl.I, wl.T, wl.k
+        w13, w2, dense_expert = _layer(0, E, H, I)
+        x = synth.activations(0, T, H, device=DEV)
+        ids, wts = synth.routing(0, T, E, k)
+    else:
+        E, H, I, T, k = (8, 512, 256, 48, 4) if case == "dup_invalid" else (8, 256, 512, 96, 2)
+        w13, w2, dense_expert = _layer(31, E, H, I, True)
+        x = synth.activations(32, T, H, device=DEV)
+        ids, wts = synth.routing(33, T, E, k)
+        if case == "dup_invalid":
+            ids[3, 1] = ids[3, 0]                        # a token naming one expert twice
+            ids[5, 2] = -1                               # a dropped pair
+            ids[7, 0] = E + 3                            # invalid ids, counted in status
+            ids[9, 3] = -5
+        else:
+            ids[:70, 0] = 0                              # expert 0: 70+ rows, three m-blocks
+            ids[:70, 1] = np.where(ids[:70, 1] == 0, 1, ids[:70, 1])
+    clean = np.where((ids < -1) | (ids >= E), -1, ids)     # invalid ids are dropped like -1
+    g13, g2 = _globals(x, clean, E, dense_expert, False)
+    (f_on, out_f, it_f), (f_off, out_u, it_u) = _ffn_both_paths(x, ids, wts, w13, w2, g13, g2)
+    assert f_on == 1 and f_off == 0
+    assert np.array_equal(out_f, out_u)
+    for key in ("counts", "offsets", "inv", "status"):
+        assert np.array_equal(it_f[key], it_u[key]), key
+    n = int(it_u["offsets"][-1])
+    assert np.array_equal(it_f["sorted"][:n], it_u["sorted"][:n])
+    live = it_u["sorted"][:n]
+    for key in ("a13_codes", "a13_scales"):
+        assert np.array_equal(it_f[key][live], it_u[key][live]), key
+    for key in ("a2_codes", "a2_scales", "down_rows"):
+        assert np.array_equal(it_f[key][:n], it_u[key][:n]), key
+    rc, ro, rs, ri = moe.permute(clean, E)
+    assert np.array_equal(it_f["offsets"], ro) and np.array_equal(it_f["inv"], ri)
+    assert int(it_f["status"][0]) == int(((ids < -1) | (ids >= E)).sum())
