@@ -143,16 +143,18 @@ moesq_status moesq_grouped_gemm(const uint8_t *a_codes, const uint8_t *a_scales,
  *   (already times the router weight) in sorted order (row inv[p]); route_scratch is the
  *   permutation's scratch.
  *   Decode sizes (tiled weights, H and I <= 2048, T*k <= 4096, mean rows per expert <= 48, and one
- *   workgroup per (expert, 384 columns of I) resident at once) can run as one cooperative launch
- *   (MOESQ_FLAG_FUSED; layout.fused = 1): same results and intermediates, except that tile_offsets and route_scratch
- *   are not written; `sync` is its barrier area (any initial contents). If a barrier wait of
- *   that launch runs out (it should not), status[0] reads -1 and the outputs are not valid. */
+ *   workgroup per (expert, 384 columns of I) resident at once) can run as one persistent launch with
+ *   grid barriers (MOESQ_FLAG_FUSED; layout.fused = 1): same results and intermediates, except that
+ *   tile_offsets and route_scratch are not written; `sync` is its barrier area (any initial
+ *   contents). It assumes the device is not busy with other work holding CUs; if a barrier wait
+ *   runs out (it should not), status[0] reads -1 and the outputs are not valid. Two fused calls on
+ *   one workspace must not overlap in time. */
 typedef struct {
   size_t counts, offsets, tile_offsets, sorted, inv, status;
   size_t a13_codes, a13_scales, a2_codes, a2_scales, down_rows, route_scratch, sync;
   size_t total;
   int32_t rows_per_mblock;   /* m-block size of the tactic the call uses */
-  int32_t fused;             /* 1: a call with tiled weights runs as one cooperative launch */
+  int32_t fused;             /* 1: a call with tiled weights runs as one persistent launch */
 } moesq_ffn_layout;
 moesq_status moesq_moe_ffn_layout(int64_t T, int32_t H, int32_t I, int32_t k, int32_t E, uint32_t flags,
                                   moesq_ffn_layout *layout /* host */);

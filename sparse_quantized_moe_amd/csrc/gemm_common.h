@@ -179,7 +179,26 @@ __device__ __forceinline__ float row_weight(const GemmParams& p, int row) { retu
 // Epilogues. Accumulator acc[rt][tt] of lane (n = lane & 15, q = lane >> 4) holds, for r = 0..3,
 // weight row wrow[rt] + 4q + r and the m-block's token row tt*16 + n. s_rw: router weights of the
 // m-block's rows (down only).
-template <int EPI, int TG, int RT = 4>
+// Stores of the epilogues. CPOL 0: plain stores. Otherwise buffer stores with that cache policy
+// (kCpolDevice: device-coherent, written through for readers in other workgroups of the same
+// launch without a cache write-back); offsets are bytes from the buffer's base (< 2^31).
+constexpr int kCpolDevice = 16;   // sc1
+
+template <int CPOL, class T>
+__device__ __forceinline__ void epi_store(T* base, int64_t idx, T v) {
+  if constexpr (CPOL == 0) {
+    base[idx] = v;
+  } else {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, 0x7FFFFFFF, kBufferRsrcWord3);
+    const uint32_t off = (uint32_t)(idx * (int64_t)sizeof(T));
+    if constexpr (sizeof(T) == 16) __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, CPOL);
+    else if constexpr (sizeof(T) == 4) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, CPOL);
+    else if constexpr (sizeof(T) == 2) __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, v), r, off, 0, CPOL);
+    else __builtin_amdgcn_raw_buffer_store_b8(__builtin_bit_cast(uint8_t, v), r, off, 0, CPOL);
+  }
+}
+
+template <int EPI, int TG, int RT = 4, int CPOL = 0>
 __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, const EpiScalars& es, f32x4 (&acc)[RT][TG],
                                               int row0, int m0, int mrows, int nb, int wv, const int* wrow,
                                               const float* s_rw, int lane) {
@@ -217,9 +236,9 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, const EpiScal
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const uint16_t v = (uint16_t)nvfp4_codes<4>(h[half], s, g2, rc);
-          *reinterpret_cast<uint16_t*>(p.h_codes + row * (I >> 1) + ((hcol0 + half * 16 + 4 * qa) >> 1)) = v;
+          epi_store<CPOL>(reinterpret_cast<uint16_t*>(p.h_codes), (row * (I >> 1) + ((hcol0 + half * 16 + 4 * qa) >> 1)) >> 1, v);
         }
-        if (qa == 0) p.h_scales[row * (I >> 5) + (hcol0 >> 5)] = (uint8_t)scb;
+        if (qa == 0) epi_store<CPOL>(p.h_scales, row * (I >> 5) + (hcol0 >> 5), (uint8_t)scb);
       }
     }
   } else {
@@ -234,7 +253,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, const EpiScal
         for (int rt = 0; rt < RT; ++rt) {
           const int col = wrow[rt] + 4 * qa;
           const float gcol = (EPI == kEpiStore && col >= (N >> 1)) ? es.g1 : gsc;
-          *reinterpret_cast<f32x4*>(p.out + row * N + col) = acc[rt][tt] * gcol;
+          epi_store<CPOL>(reinterpret_cast<f32x4*>(p.out), (row * N + col) >> 2, acc[rt][tt] * gcol);
         }
       }
     }

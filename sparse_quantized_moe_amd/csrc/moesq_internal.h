@@ -75,7 +75,7 @@ struct GemmParams {
 };
 void launch_grouped_gemm(const GemmParams& p, int epi, int tactic, hipStream_t stream);
 
-// Decode-size FFN in one cooperative launch (ffn_fused.hip): tiled weights, H, I <= 2048,
+// Decode-size FFN in one persistent launch (ffn_fused.hip): tiled weights, H, I <= 2048,
 // T*k <= 4096, and every (expert, part) workgroup resident at once.
 struct FusedLaunch {
   const uint16_t* x;
