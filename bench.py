@@ -333,7 +333,7 @@ def main():
             "workload": pw.name, "tokens": pw.T, "value": round(eff, 2), "unit": "effective dense TFLOP/s",
             "ms_per_step": round(pwall / psteps * 1e3, 4), "steps": psteps,
             "stage_ms": {n: round(float(v), 4) for n, v in zip(moesq.FFN_STAGES, pst_mean)},
-            "roofline": {"bound": "mfma", "kernel": "k_grouped_gemm<gate_up> (prefill tactic)",
+            "roofline": {"bound": "mfma", "kernel": "k_gemm_prefill<gate_up>",
                          "achieved": round(ach, 2), "peak": F16_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(ach / F16_DENSE_PEAK_TFLOPS, 4), "traffic": None,
                          "algorithmic_flops_per_launch": alg_flops, "avg_launch_ms": round(g_ms, 4)},
