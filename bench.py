@@ -147,6 +147,35 @@ def run_steps(moesq, torch, ev, x, ids_t, wts_t, layers, g13_t, g2_t, out, ws, w
     return wall, stages, gpu_ms
 
 
+def measured_peaks(moesq, torch, ev):
+    """What this GPU sustains, beside the published peaks: a plain 1 GiB device copy (read + write
+    bytes per second) and the library's probe of v_smfmac_f32_16x16x64_f16 (kept-half FLOP/s: 16384
+    per instruction), both timed with HIP events on the current stream."""
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    e = ev.create(2)
+    for _ in range(2):
+        dst.copy_(src)
+    ev.record(e[0])
+    for _ in range(5):
+        dst.copy_(src)
+    ev.record(e[1])
+    torch.cuda.synchronize()
+    copy_gbs = 2 * n * 5 / (ev.elapsed_ms(e[0], e[1]) * 1e-3) / 1e9
+    del src, dst
+    blocks = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    moesq.probe_smfmac(blocks, 256, sink)
+    ev.record(e[0])
+    insts = moesq.probe_smfmac(blocks, 4096, sink)
+    ev.record(e[1])
+    torch.cuda.synchronize()
+    tf = insts * 16384 / (ev.elapsed_ms(e[0], e[1]) * 1e-3) / 1e12
+    ev.destroy(e)
+    return {"copy_GBps": round(copy_gbs, 1), "smfmac_f16_kept_TFLOPs": round(tf, 1)}
+
+
 def cpu_baseline(wl, seed, x, ids, wts, g13, g2, dense_expert, ntok):
     """The oracle (unchanged) on a bounded sample of the decode batch: ntok tokens and their experts."""
     import multiprocessing
@@ -223,6 +252,8 @@ def main():
         torch.cuda.synchronize()
         log(f"copy calibration: 3 copies of {n} bytes")
         del src, dst
+    peaks = measured_peaks(moesq, torch, ev)
+    log(f"measured: device copy {peaks['copy_GBps']} GB/s, smfmac f16 {peaks['smfmac_f16_kept_TFLOPs']} TFLOP/s (kept half)")
     wl = synth.WORKLOADS[args.workload]
     w13, w2, dense_expert = build_layer(wl, args.seed, dev)
     layers = [(w13, w2)]
@@ -303,7 +334,9 @@ def main():
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": kbytes,
-                     "avg_launch_us": round(k_ms * 1e3, 2)},
+                     "avg_launch_us": round(k_ms * 1e3, 2),
+                     "measured_peak": peaks["copy_GBps"], "frac_of_measured": round(achieved / peaks["copy_GBps"], 4)},
+        "measured_peaks": peaks,
     }
     del layers[1:]
     torch.cuda.empty_cache()
@@ -336,7 +369,9 @@ def main():
             "roofline": {"bound": "mfma", "kernel": "k_gemm_prefill<gate_up>",
                          "achieved": round(ach, 2), "peak": F16_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(ach / F16_DENSE_PEAK_TFLOPS, 4), "traffic": None,
-                         "algorithmic_flops_per_launch": alg_flops, "avg_launch_ms": round(g_ms, 4)},
+                         "algorithmic_flops_per_launch": alg_flops, "avg_launch_ms": round(g_ms, 4),
+                         "measured_peak": peaks["smfmac_f16_kept_TFLOPs"],
+                         "frac_of_measured": round(ach / peaks["smfmac_f16_kept_TFLOPs"], 4)},
         }
 
     if not args.no_cpu_baseline:

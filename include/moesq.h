@@ -172,6 +172,15 @@ moesq_status moesq_moe_ffn(const void *x, int64_t T, int32_t H, const int32_t *t
  * The library keeps the pointer (thread-local) until it is reset; the caller keeps the array alive. */
 moesq_status moesq_set_stage_events(hipEvent_t *events /* host */, int32_t n);
 
+/* Measurement aid: a throughput probe of v_smfmac_f32_16x16x64_f16, the instruction the grouped GEMMs
+ * are built on, so rooflines can be quoted against the rate this GPU sustains besides the published
+ * peak. Launches `blocks` workgroups of 4 waves, each wave issuing iters x 8 independent instructions
+ * (16 x 16 outputs, 64 dense K: 16384 multiply-adds on the kept half); time it with events on
+ * `stream`. sink: blocks * 256 floats (device, written). *n_insts (host): instructions issued.
+ * blocks >= 1, iters >= 1. */
+moesq_status moesq_probe_smfmac(int32_t blocks, int32_t iters, float *sink, int64_t *n_insts /* host */,
+                                hipStream_t stream);
+
 /* Weight compression of a dense fp32 linear [N][K] into pair-bitmask NVFP4 (the synthetic-layer
  * recipe; model card "Compression details": paired 4:8 along K, 2 of every 4 pairs kept): in each
  * 8-K chunk keep the 2 pairs with the largest a*a + b*b (float64, ties to the lower pair),

@@ -35,7 +35,7 @@ EXPORTED_SYMBOLS = (
     "moesq_grouped_gemm_workspace_size", "moesq_grouped_gemm", "moesq_moe_ffn_layout",
     "moesq_moe_ffn_workspace_size", "moesq_moe_ffn", "moesq_compress_weights", "moesq_validate_weights",
     "moesq_unpack_pair_bitmask", "moesq_pack_pair_bitmask", "moesq_set_stage_events", "moesq_tiled_bytes",
-    "moesq_prepare_weights", "moesq_unprepare_weights", "moesq_permute_workspace_size",
+    "moesq_prepare_weights", "moesq_unprepare_weights", "moesq_permute_workspace_size", "moesq_probe_smfmac",
 )
 
 
@@ -83,6 +83,7 @@ def _declare(L: ctypes.CDLL) -> None:
         "moesq_unpack_pair_bitmask": (ctypes.c_int, [_P, _P, _I64, _I32, _P, _P, _P]),
         "moesq_pack_pair_bitmask": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _P, _P]),
         "moesq_set_stage_events": (ctypes.c_int, [_P, _I32]),
+        "moesq_probe_smfmac": (ctypes.c_int, [_I32, _I32, _P, ctypes.POINTER(_I64), _P]),
         "moesq_tiled_bytes": (_SZ, [_I32, _I32, _I32]),
         "moesq_prepare_weights": (ctypes.c_int, [ctypes.POINTER(_CWeights), _P, _P]),
         "moesq_unprepare_weights": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _P, _P, _P]),
@@ -356,7 +357,18 @@ def set_stage_events(events) -> None:
         _check(lib().moesq_set_stage_events(ctypes.cast(events, ctypes.c_void_p), len(events)))
 
 
-__all__ += ["FFN_STAGES", "set_stage_events"]
+__all__ += ["FFN_STAGES", "set_stage_events", "probe_smfmac"]
+
+
+def probe_smfmac(blocks: int, iters: int, sink: torch.Tensor) -> int:
+    """Launch the v_smfmac_f32_16x16x64_f16 throughput probe on the current stream (see
+    moesq_probe_smfmac); returns the number of instructions issued. sink: >= blocks*256 fp32 on device."""
+    if sink.numel() < blocks * 256:
+        raise MoesqError(-1, "probe_smfmac: sink too small")
+    n = ctypes.c_int64()
+    _check(lib().moesq_probe_smfmac(blocks, iters, _dev(sink, "sink", torch.float32), ctypes.byref(n),
+                                    _stream()))
+    return n.value
 
 
 def validate_weights(mask: torch.Tensor, K: int) -> int:

@@ -92,6 +92,13 @@ moesq_status moesq_set_stage_events(hipEvent_t* events, int32_t n) {
   return MOESQ_OK;
 }
 
+moesq_status moesq_probe_smfmac(int32_t blocks, int32_t iters, float* sink, int64_t* n_insts, hipStream_t stream) {
+  MOESQ_REQUIRE(blocks >= 1 && iters >= 1 && sink && n_insts, MOESQ_ERR_INVALID,
+                "probe_smfmac: blocks >= 1, iters >= 1, sink and n_insts required");
+  *n_insts = moesq::launch_probe_smfmac(blocks, iters, sink, stream);
+  return check_launch(stream, false);
+}
+
 moesq_status moesq_quantize_act(const void* x, moesq_dtype x_dtype, int64_t rows, int32_t K, int64_t x_row_stride,
                                 const int32_t* src_row, const int32_t* expert_offsets, int32_t E, const float* global,
                                 uint8_t* codes, uint8_t* scales, hipStream_t stream) {

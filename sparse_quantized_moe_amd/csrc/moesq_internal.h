@@ -106,6 +106,9 @@ constexpr size_t kFusedSyncBytes = 64 + 8 * 1024;
 bool fused_applicable(int64_t T, int H, int I, int k, int E);
 hipError_t launch_ffn_fused(const FusedLaunch& f, hipStream_t stream);
 
+// smfmac throughput probe (probe.hip): returns the number of instructions the launch issues.
+int64_t launch_probe_smfmac(int blocks, int iters, float* sink, hipStream_t stream);
+
 // out[t][:] = sum_j D[inv[t*k + j]][:] (rows with inv < 0 skipped), in j order.
 void launch_combine(const float* D, const int* inv, int64_t T, int k, int H, float* out, hipStream_t stream);
 
