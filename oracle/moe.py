@@ -38,6 +38,27 @@ def permute(topk_ids, E: int):
     return counts.astype(np.int64), offsets.astype(np.int64), sorted_pairs.astype(np.int64), inv
 
 
+def route_topk(logits, k: int, renormalize: bool = True):
+    """Router of a MoE layer (the BF16 `mlp.gate` the model cards leave uncompressed; the pages do not
+    spell its rule, the reading taken is the usual softmax top-k): probabilities p = softmax(logits)
+    over the E experts in float64, the k largest p per token, equal p going to the lower expert id,
+    listed by decreasing p; their weights are p renormalized over the k picks when ``renormalize``,
+    else p itself.
+
+    logits [T, E] -> ids int64 [T, k], weights float64 [T, k].
+    """
+    z = np.asarray(logits, dtype=np.float64)
+    if z.ndim != 2 or not 1 <= k <= z.shape[1]:
+        raise ValueError("logits [T, E] with 1 <= k <= E")
+    e = np.exp(z - z.max(axis=1, keepdims=True))
+    p = e / e.sum(axis=1, keepdims=True)
+    ids = np.argsort(-p, axis=1, kind="stable")[:, :k]        # stable: equal p keep id order
+    w = np.take_along_axis(p, ids, axis=1)
+    if renormalize:
+        w = w / w.sum(axis=1, keepdims=True)
+    return ids.astype(np.int64), w
+
+
 def weight_rows_global(gw_e, N: int) -> np.ndarray:
     """Per-row weight global of one expert linear: G=1 -> all rows; G=2 -> rows [0,N/2) take gw[0]
     (gate), rows [N/2,N) take gw[1] (up)."""

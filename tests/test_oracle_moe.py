@@ -136,3 +136,44 @@ def test_synth_routing_shapes():
     assert counts.max() > 5 * counts.mean() and (counts == 0).sum() >= 1
     assert np.allclose(wts.sum(axis=1), 1, atol=1e-6)
     assert (np.diff(np.sort(ids, axis=1), axis=1) > 0).all()        # distinct experts per token
+
+
+# ---- router (route_topk) pins: the selection against a rank definition counted pair by pair, the
+# weights against closed forms
+
+def _rank_select(l, k):
+    """Experts of one token by a counting definition: rank_i = #{j : l_j > l_i, or l_j == l_i and j < i}."""
+    E = len(l)
+    rank = [sum(1 for j in range(E) if l[j] > l[i] or (l[j] == l[i] and j < i)) for i in range(E)]
+    return [i for r in range(k) for i in range(E) if rank[i] == r]
+
+
+def test_route_topk_selection_vs_rank_count():
+    rng = np.random.default_rng(5)
+    for E, k in ((6, 2), (9, 4), (16, 16), (33, 8)):
+        l = rng.integers(-3, 4, size=(20, E)).astype(np.float64)      # many equal logits
+        ids, w = moe.route_topk(l, k)
+        for t in range(20):
+            assert ids[t].tolist() == _rank_select(l[t].tolist(), k)
+        assert np.all(np.diff(w, axis=1) <= 0)                         # listed by decreasing weight
+
+
+def test_route_topk_weights_closed_forms():
+    rng = np.random.default_rng(6)
+    l = rng.standard_normal((50, 12))
+    ids, w = moe.route_topk(l, 4)
+    sel = np.take_along_axis(l, ids, axis=1)
+    assert np.allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-15)
+    # ratios of weights are exp(differences of logits), whatever the normalization
+    assert np.allclose(w[:, 1:] / w[:, :1], np.exp(sel[:, 1:] - sel[:, :1]), rtol=1e-13)
+    # without renormalization the weights are the softmax probabilities: all of them sum to 1
+    ids_all, p_all = moe.route_topk(l, 12, renormalize=False)
+    assert np.allclose(p_all.sum(axis=1), 1.0, rtol=0, atol=1e-15)
+    _, p4 = moe.route_topk(l, 4, renormalize=False)
+    assert np.allclose(p4, p_all[:, :4], rtol=0, atol=0)
+    # equal logits: the first k ids, weight 1/k each
+    ids_eq, w_eq = moe.route_topk(np.full((3, 10), 0.7), 3)
+    assert ids_eq.tolist() == [[0, 1, 2]] * 3 and np.allclose(w_eq, 1.0 / 3, rtol=0, atol=1e-16)
+    # a shift of all logits of a token changes nothing
+    ids_s, w_s = moe.route_topk(l + 123.25, 4)
+    assert np.array_equal(ids_s, ids) and np.allclose(w_s, w, rtol=1e-12)
