@@ -176,6 +176,38 @@ def measured_peaks(moesq, torch, ev):
     return {"copy_GBps": round(copy_gbs, 1), "smfmac_f16_kept_TFLOPs": round(tf, 1)}
 
 
+def router_figures(moesq, torch, ev, reps=50):
+    """The router kernel that feeds the permutation (softmax top-k over bf16 logits), timed with HIP
+    events over back-to-back calls at the decode and the largest prefill shape; bytes = logits in +
+    ids and weights out."""
+    res = {}
+    for name, T, E, k in (("decode_T256_E128_k8", 256, 128, 8), ("prefill_T16384_E384_k8", 16384, 384, 8)):
+        g = torch.Generator(device="cuda").manual_seed(T + E)
+        logits = torch.randn((T, E), generator=g, device="cuda").to(torch.bfloat16)
+        ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+        w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+        for _ in range(3):
+            moesq.route_topk(logits, k, out_ids=ids, out_weights=w)
+        # the calls queue up behind a long matmul, so the GPU runs them back to back whatever the
+        # host's launch rate (each call's time then includes the gap between dependent launches)
+        a = torch.randn((8192, 8192), device="cuda", dtype=torch.bfloat16)
+        e = ev.create(2)
+        torch.cuda.synchronize()
+        _ = a @ a
+        ev.record(e[0])
+        for _ in range(reps):
+            moesq.route_topk(logits, k, out_ids=ids, out_weights=w)
+        ev.record(e[1])
+        torch.cuda.synchronize()
+        us = ev.elapsed_ms(e[0], e[1]) / reps * 1e3
+        ev.destroy(e)
+        del a
+        nbytes = T * E * 2 + T * k * 8
+        res[name] = {"us_per_call": round(us, 2), "tokens_per_s": round(T / (us * 1e-6), 0),
+                     "GBps": round(nbytes / (us * 1e-6) / 1e9, 1), "bytes": nbytes}
+    return res
+
+
 def cpu_baseline(wl, seed, x, ids, wts, g13, g2, dense_expert, ntok):
     """The oracle (unchanged) on a bounded sample of the decode batch: ntok tokens and their experts."""
     import multiprocessing
@@ -337,6 +369,7 @@ def main():
                      "avg_launch_us": round(k_ms * 1e3, 2),
                      "measured_peak": peaks["copy_GBps"], "frac_of_measured": round(achieved / peaks["copy_GBps"], 4)},
         "measured_peaks": peaks,
+        "router": router_figures(moesq, torch, ev),
     }
     del layers[1:]
     torch.cuda.empty_cache()

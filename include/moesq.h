@@ -165,6 +165,18 @@ moesq_status moesq_moe_ffn(const void *x, int64_t T, int32_t H, const int32_t *t
                            float *out, void *workspace, size_t workspace_bytes, uint32_t flags,
                            hipStream_t stream);
 
+/* Router of the MoE layer (the step that feeds the permutation): per token t, softmax over the E
+ * expert logits, the k most probable experts (equal probability: the lower expert id first), listed
+ * by decreasing probability, and their weights: the probabilities renormalized over the k picks
+ * (renormalize != 0) or the softmax probabilities themselves. The model cards keep this router
+ * (`mlp.gate`) in BF16 ahead of the compressed experts (model card "Qwen3.5-397B-A17B-P48NVFP4-MoESQ",
+ * "Compression details"); the softmax top-k rule is the usual one, the pages do not spell it out.
+ *   logits [T][E] bf16 or fp32 (finite); topk_ids int32 [T][k], topk_weights fp32 [T][k] out.
+ *   The picks compare the logits exactly; the weights are computed in fp32 (within 1e-6 relative of
+ *   the exact softmax). E <= 1024, 1 <= k <= min(E, 64); T = 0 is a no-op. */
+moesq_status moesq_route_topk(const void *logits, moesq_dtype dtype, int64_t T, int32_t E, int32_t k,
+                              int32_t renormalize, int32_t *topk_ids, float *topk_weights, hipStream_t stream);
+
 /* Profiling aid: with events (host array of n >= 5 hipEvent_t created by the caller) set, every later
  * moesq_moe_ffn call on this host thread records events[0] on its stream before its first kernel and
  * events[1..4] after the routing (permutation and gate/up input quantization), the gate/up GEMM (with

@@ -18,13 +18,15 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "MoesqError", "SparseWeights", "lib", "library_path", "abi_version", "quantize_act", "permute",
+    "MoesqError", "SparseWeights", "lib", "library_path", "abi_version", "ABI_VERSION", "quantize_act", "permute",
     "grouped_gemm", "moe_ffn", "ffn_layout", "compress_weights", "compress_moe_layer", "validate_weights",
     "pack_pair_bitmask", "unpack_pair_bitmask", "FLAG_SYNC_CHECK", "FLAG_UNFUSED", "FLAG_FUSED", "EXPORTED_SYMBOLS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_PKG, "libmoesq.so")
+#: The C ABI version (MOESQ_ABI_VERSION in include/moesq.h) these bindings are declared for.
+ABI_VERSION = 4
 FLAG_SYNC_CHECK = 1
 FLAG_UNFUSED = 2      # moe_ffn: separate launches even where the one-launch decode path applies
 FLAG_FUSED = 4        # moe_ffn: the one-launch decode path wherever it applies
@@ -36,6 +38,7 @@ EXPORTED_SYMBOLS = (
     "moesq_moe_ffn_workspace_size", "moesq_moe_ffn", "moesq_compress_weights", "moesq_validate_weights",
     "moesq_unpack_pair_bitmask", "moesq_pack_pair_bitmask", "moesq_set_stage_events", "moesq_tiled_bytes",
     "moesq_prepare_weights", "moesq_unprepare_weights", "moesq_permute_workspace_size", "moesq_probe_smfmac",
+    "moesq_route_topk",
 )
 
 
@@ -84,6 +87,7 @@ def _declare(L: ctypes.CDLL) -> None:
         "moesq_pack_pair_bitmask": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _P, _P]),
         "moesq_set_stage_events": (ctypes.c_int, [_P, _I32]),
         "moesq_probe_smfmac": (ctypes.c_int, [_I32, _I32, _P, ctypes.POINTER(_I64), _P]),
+        "moesq_route_topk": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I32, _I32, _I32, _P, _P, _P]),
         "moesq_tiled_bytes": (_SZ, [_I32, _I32, _I32]),
         "moesq_prepare_weights": (ctypes.c_int, [ctypes.POINTER(_CWeights), _P, _P]),
         "moesq_unprepare_weights": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _P, _P, _P]),
@@ -102,6 +106,9 @@ def lib() -> ctypes.CDLL:
             raise MoesqError(f"{library_path} is missing: build it with `python -m sparse_quantized_moe_amd.build`")
         L = ctypes.CDLL(library_path)
         _declare(L)
+        if L.moesq_abi_version() != ABI_VERSION:
+            raise MoesqError(f"{library_path} has C ABI {L.moesq_abi_version()}, these bindings expect "
+                             f"{ABI_VERSION}: rebuild it with `python -m sparse_quantized_moe_amd.build`")
         _lib = L
     return _lib
 
@@ -357,14 +364,30 @@ def set_stage_events(events) -> None:
         _check(lib().moesq_set_stage_events(ctypes.cast(events, ctypes.c_void_p), len(events)))
 
 
-__all__ += ["FFN_STAGES", "set_stage_events", "probe_smfmac"]
+__all__ += ["FFN_STAGES", "set_stage_events", "probe_smfmac", "route_topk"]
+
+
+def route_topk(logits: torch.Tensor, k: int, renormalize: bool = True, out_ids: Optional[torch.Tensor] = None,
+               out_weights: Optional[torch.Tensor] = None):
+    """Router softmax top-k (see moesq_route_topk): logits [T, E] bf16 or fp32 on the device ->
+    (topk_ids int32 [T, k], topk_weights fp32 [T, k])."""
+    T, E = logits.shape
+    if logits.dtype not in (torch.bfloat16, torch.float32):
+        raise MoesqError("route_topk: logits must be bf16 or fp32")
+    dtype = 1 if logits.dtype == torch.float32 else 0
+    ids = out_ids if out_ids is not None else torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    wts = out_weights if out_weights is not None else torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _check(lib().moesq_route_topk(_dev(logits, "logits", logits.dtype), dtype, T, E, k, 1 if renormalize else 0,
+                                  _dev(ids, "topk_ids", torch.int32), _dev(wts, "topk_weights", torch.float32),
+                                  _stream()))
+    return ids, wts
 
 
 def probe_smfmac(blocks: int, iters: int, sink: torch.Tensor) -> int:
     """Launch the v_smfmac_f32_16x16x64_f16 throughput probe on the current stream (see
     moesq_probe_smfmac); returns the number of instructions issued. sink: >= blocks*256 fp32 on device."""
     if sink.numel() < blocks * 256:
-        raise MoesqError(-1, "probe_smfmac: sink too small")
+        raise MoesqError("probe_smfmac: sink too small")
     n = ctypes.c_int64()
     _check(lib().moesq_probe_smfmac(blocks, iters, _dev(sink, "sink", torch.float32), ctypes.byref(n),
                                     _stream()))

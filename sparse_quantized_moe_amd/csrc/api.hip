@@ -92,6 +92,17 @@ moesq_status moesq_set_stage_events(hipEvent_t* events, int32_t n) {
   return MOESQ_OK;
 }
 
+moesq_status moesq_route_topk(const void* logits, moesq_dtype dtype, int64_t T, int32_t E, int32_t k,
+                              int32_t renormalize, int32_t* topk_ids, float* topk_weights, hipStream_t stream) {
+  MOESQ_REQUIRE(T >= 0 && E >= 1 && E <= 1024 && k >= 1 && k <= E && k <= 64, MOESQ_ERR_INVALID,
+                "route_topk: T >= 0, 1 <= E <= 1024, 1 <= k <= min(E, 64)");
+  MOESQ_REQUIRE(dtype == MOESQ_BF16 || dtype == MOESQ_F32, MOESQ_ERR_INVALID, "route_topk: bad dtype");
+  if (T == 0) return MOESQ_OK;
+  MOESQ_REQUIRE(logits && topk_ids && topk_weights, MOESQ_ERR_INVALID, "route_topk: null pointer");
+  moesq::launch_route_topk(logits, dtype == MOESQ_F32, T, E, k, renormalize != 0, topk_ids, topk_weights, stream);
+  return check_launch(stream, false);
+}
+
 moesq_status moesq_probe_smfmac(int32_t blocks, int32_t iters, float* sink, int64_t* n_insts, hipStream_t stream) {
   MOESQ_REQUIRE(blocks >= 1 && iters >= 1 && sink && n_insts, MOESQ_ERR_INVALID,
                 "probe_smfmac: blocks >= 1, iters >= 1, sink and n_insts required");

@@ -106,6 +106,10 @@ constexpr size_t kFusedSyncBytes = 64 + 8 * 1024;
 bool fused_applicable(int64_t T, int H, int I, int k, int E);
 hipError_t launch_ffn_fused(const FusedLaunch& f, hipStream_t stream);
 
+// Router softmax top-k (router.hip): E <= 1024, 1 <= k <= min(E, 64).
+void launch_route_topk(const void* logits, bool f32, int64_t T, int E, int k, bool renormalize, int* ids,
+                       float* wts, hipStream_t stream);
+
 // smfmac throughput probe (probe.hip): returns the number of instructions the launch issues.
 int64_t launch_probe_smfmac(int blocks, int iters, float* sink, hipStream_t stream);
 

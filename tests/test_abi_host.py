@@ -29,7 +29,9 @@ def test_every_declared_symbol_is_exported():
     for name in decl:
         assert hasattr(L, name), name
     assert sorted(decl) == sorted(moesq.EXPORTED_SYMBOLS)
-    assert moesq.abi_version() == 4
+    hdr = open(os.path.join(ROOT, "include", "moesq.h")).read()
+    declared = int(re.search(r"#define MOESQ_ABI_VERSION (\d+)", hdr).group(1))
+    assert moesq.abi_version() == moesq.ABI_VERSION == declared
 
 
 def test_status_strings():
@@ -91,6 +93,14 @@ def test_argument_checks_return_status_without_launching():
     assert L.moesq_moe_ffn(*args(_weights(E=E, N=2 * I, K=H, G=1), w2, 1 << 30)) == INVALID
     assert L.moesq_moe_ffn(*args(w13, w2, 16)) == WORKSPACE
     assert L.moesq_moe_ffn(P, 0, H, P, P, 2, ctypes.byref(w13), ctypes.byref(w2), P, P, P, P, 16, 0, None) == OK
+    # router: k out of range, too many experts, bad dtype, null outputs; no tokens is a no-op
+    assert L.moesq_route_topk(P, 0, 4, 8, 9, 1, P, P, None) == INVALID
+    assert L.moesq_route_topk(P, 0, 4, 128, 65, 1, P, P, None) == INVALID
+    assert L.moesq_route_topk(P, 0, 4, 1025, 8, 1, P, P, None) == INVALID
+    assert L.moesq_route_topk(P, 7, 4, 8, 2, 1, P, P, None) == INVALID
+    assert L.moesq_route_topk(P, 0, 4, 8, 2, 1, None, P, None) == INVALID
+    assert b"null pointer" in L.moesq_last_error()
+    assert L.moesq_route_topk(None, 0, 0, 8, 2, 1, None, None, None) == OK
     # compress and codec
     assert L.moesq_compress_weights(P, 4, 40, P, P, P, P, None) == INVALID
     assert L.moesq_validate_weights(P, 4, 40, P, None) == INVALID
