@@ -172,8 +172,10 @@ moesq_status moesq_moe_ffn(const void *x, int64_t T, int32_t H, const int32_t *t
  * (`mlp.gate`) in BF16 ahead of the compressed experts (model card "Qwen3.5-397B-A17B-P48NVFP4-MoESQ",
  * "Compression details"); the softmax top-k rule is the usual one, the pages do not spell it out.
  *   logits [T][E] bf16 or fp32 (finite); topk_ids int32 [T][k], topk_weights fp32 [T][k] out.
- *   The picks compare the logits exactly; the weights are computed in fp32 (within 1e-6 relative of
- *   the exact softmax). E <= 1024, 1 <= k <= min(E, 64); T = 0 is a no-op. */
+ *   The picks compare the logits exactly; the weights are computed in fp32, within
+ *   (2*S + log2(n) + n/64 + 16) * 2^-24 relative of the exact value (S: the token's max - min logit,
+ *   n: the softmax terms, k or E). E <= 1024, 1 <= k <= min(E, 64); T = 0 is a no-op. Errors: a
+ *   negative status for arguments out of range or a null pointer, nothing enqueued. */
 moesq_status moesq_route_topk(const void *logits, moesq_dtype dtype, int64_t T, int32_t E, int32_t k,
                               int32_t renormalize, int32_t *topk_ids, float *topk_weights, hipStream_t stream);
 
