@@ -70,6 +70,34 @@ def weight_rows_global(gw_e, N: int) -> np.ndarray:
     raise ValueError("G must be 1, or 2 with N even")
 
 
+def fold_gate_up_globals(scale13, gw13):
+    """Load-time fold of the gate/up global ratio into the block scales (model card
+    "Qwen3.8-Flash-Next-P48NVFP4-MoESQ", the note under "Compression details", and model card
+    "Qwen3-30B-A3B-P48NVFP4-MoESQ", the note after the evaluation table: the two projections carry
+    separate globals, and the serving loader folds their ratio into the block scales so that one
+    global serves both). Reading: the gate's global is the one kept for both halves (the one a loader
+    without the fold would apply to both), and each up block scale s becomes the E4M3 code nearest to
+    e4m3(s) * r (ties to even, saturating at 448), r = the fp32 quotient g_up / g_gate; a zero scale
+    stays zero. e4m3(s) has 4 significant bits and r 24, so the product is exact in float64.
+
+    scale13 u8 [2I, K/32] (gate rows, then up rows), gw13 [2] -> (scale u8 [2I, K/32], gw float32 [2]).
+    """
+    scale13 = np.asarray(scale13, dtype=np.uint8)
+    gw13 = np.asarray(gw13, dtype=np.float32).ravel()
+    N = scale13.shape[0]
+    if gw13.shape[0] != 2 or N % 2:
+        raise ValueError("a fused gate|up linear: 2 globals and an even number of rows")
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.float64(np.float32(np.float64(gw13[1]) / np.float64(gw13[0])))
+    up = scale13[N // 2:]
+    with np.errstate(invalid="ignore"):
+        v = nvfp4.e4m3fn_decode(up) * r
+    folded = np.where(up == 0, np.uint8(0), nvfp4.e4m3_rne_sat(np.where(up == 0, 0.0, v)))
+    out = scale13.copy()
+    out[N // 2:] = folded
+    return out, np.array([gw13[0], gw13[0]], dtype=np.float32)
+
+
 def dequant_weight(packed, mask, scale, gw_e) -> np.ndarray:
     """One expert linear in pair-bitmask NVFP4 -> dense float64 [N, K]."""
     dense = pairbitmask.unpack(packed, mask)

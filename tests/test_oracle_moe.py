@@ -177,3 +177,73 @@ def test_route_topk_weights_closed_forms():
     # a shift of all logits of a token changes nothing
     ids_s, w_s = moe.route_topk(l + 123.25, 4)
     assert np.array_equal(ids_s, ids) and np.allclose(w_s, w, rtol=1e-12)
+
+
+def _nearest_e4m3_brute(v: Fraction) -> int:
+    """The finite E4M3FN byte (0x00..0x7E) nearest to v >= 0 by exact rational distance, ties to the
+    even byte (the byte's low bit is the mantissa's)."""
+    best = None
+    for c in range(0x7F):
+        d = abs(Fraction(float(nvfp4.e4m3fn_decode(np.uint8(c)))) - v)
+        if best is None or d < best[0] or (d == best[0] and c % 2 == 0):
+            best = (d, c)
+    return best[1]
+
+
+def _fp32_nearest(q: Fraction) -> np.float32:
+    """The fp32 nearest to the positive rational q (ties to even), found among neighbours."""
+    c = np.float32(float(q))
+    cands = [np.nextafter(c, np.float32(0)), c, np.nextafter(c, np.float32(np.inf))]
+    dist = [abs(Fraction(float(x)) - q) for x in cands]
+    best = min(dist)
+    picks = [x for x, d in zip(cands, dist) if d == best]
+    return picks[0] if len(picks) == 1 else [x for x in picks if int(x.view(np.uint32)) % 2 == 0][0]
+
+
+@pytest.mark.parametrize("gg,gu", [(1.0, 3.0), (3.0, 1.0), (1e-3, 7.3e-1), (0.37, 0.0021), (2.5e-4, 2.5e-4 * 1.0001)])
+def test_fold_gate_up_globals_vs_brute_force(gg, gu):
+    """Every folded up scale is the nearest E4M3 to e4m3(s) * fp32(g_up / g_gate), by exact rationals
+    over all finite codes (ratios far from 1 reach both saturation at 448 and underflow to 0)."""
+    rng = np.random.default_rng(int(gu * 1e6) % 1000)
+    I, G = 16, 8
+    scale = rng.integers(0, 0x7F, size=(2 * I, G), dtype=np.uint8)
+    scale[I, :4] = [0x00, 0x01, 0x7E, 0x08]                   # zero, smallest subnormal, 448, 2^-6
+    gw = np.array([gg, gu], np.float32)
+    out, gw2 = moe.fold_gate_up_globals(scale, gw)
+    assert np.array_equal(out[:I], scale[:I])                 # gate rows untouched
+    assert gw2.dtype == np.float32 and gw2[0] == gw[0] and gw2[1] == gw[0]
+    r = _fp32_nearest(Fraction(float(gw[1])) / Fraction(float(gw[0])))
+    for (i, j), s in np.ndenumerate(scale[I:]):
+        v = Fraction(float(nvfp4.e4m3fn_decode(s))) * Fraction(float(r))
+        want = 0 if s == 0 else _nearest_e4m3_brute(v)
+        assert out[I + i, j] == want, (i, j, int(s), float(v))
+
+
+def test_fold_gate_up_globals_identities():
+    """Equal globals: nothing changes. A power-of-two ratio keeping every scale in E4M3's normal range:
+    the dequantized weights, and so the FFN, are exactly those of the unfolded layer."""
+    E, H, I, T, k = 3, 64, 32, 8, 2
+    w13, w2 = _tiny_layer(11, E, H, I)
+    for e in range(E):
+        same = np.array([w13[3][e][0], w13[3][e][0]], np.float32)
+        out, gw = moe.fold_gate_up_globals(w13[2][e], same)
+        assert np.array_equal(out, w13[2][e]) and np.array_equal(gw, same)
+    # rebuild the up half with globals 4x the gate's and scales in [2^-4, 112] (no saturation or
+    # subnormals after a x4 fold)
+    rng = np.random.default_rng(12)
+    f13 = [a.copy() for a in w13]
+    for e in range(E):
+        up = f13[2][e][I:]
+        up[...] = rng.integers(0x18, 0x6E, size=up.shape, dtype=np.uint8)   # 2^-4 .. 112
+        f13[3][e] = np.array([w13[3][e][0], w13[3][e][0] * 4], np.float32)
+    g13 = np.full(E, np.float32(0.002), np.float32)
+    g2 = np.full(E, np.float32(0.0005), np.float32)
+    x = synth.activations(4, T, H).float().numpy()
+    ids, wts = synth.routing(5, T, E, k)
+    ref = moe.moe_ffn(x, ids, wts, f13, w2, g13, g2)
+    folded = [a.copy() for a in f13]
+    for e in range(E):
+        folded[2][e], folded[3][e] = moe.fold_gate_up_globals(f13[2][e], f13[3][e])
+        assert np.array_equal(moe.dequant_weight(*(a[e] for a in folded)),
+                              moe.dequant_weight(*(a[e] for a in f13)))
+    assert np.array_equal(moe.moe_ffn(x, ids, wts, folded, w2, g13, g2), ref)
