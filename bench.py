@@ -208,6 +208,49 @@ def router_figures(moesq, torch, ev, reps=50):
     return res
 
 
+def fold_figures(moesq, torch, ev, reps=20):
+    """The load-time gate/up global fold (in place on the up block scales), timed with HIP events over
+    back-to-back calls at the decode layer and the largest layer; each call gets globals of its own,
+    and the calls rotate over enough copies of the scales (>= 768 MB of up scales) that they are
+    not served from the 256 MB last-level cache, as a fold at load time is not.
+    bytes = the up scales read and written + the globals."""
+    res = {}
+    for name, E, H, I in (("E128_H2048_I768", 128, 2048, 768), ("E384_H7168_I2048", 384, 7168, 2048)):
+        N, K = 2 * I, H
+        up_bytes = E * I * (K // 32)
+        copies = min(64, max(2, -(-768 * 2 ** 20 // up_bytes)))
+        g = torch.Generator(device="cuda").manual_seed(E + H)
+        scales = [torch.randint(0, 0x7F, (E, N, K // 32), generator=g, device="cuda", dtype=torch.uint8)
+                  for _ in range(copies)]
+        gw = torch.rand((reps + 3, E, 2), generator=g, device="cuda") + 0.5
+        P = moesq.lib().moesq_fold_gate_up_globals
+        stream = torch.cuda.current_stream().cuda_stream
+
+        def call(i):
+            st = P(scales[i % copies].data_ptr(), gw[i].data_ptr(), E, N, K, stream)
+            if st != 0:
+                raise RuntimeError(f"fold_gate_up_globals: status {st}")
+        for i in range(3):
+            call(reps + i)
+        a = torch.randn((8192, 8192), device="cuda", dtype=torch.bfloat16)
+        e = ev.create(2)
+        torch.cuda.synchronize()
+        _ = a @ a
+        ev.record(e[0])
+        for i in range(reps):
+            call(i)
+        ev.record(e[1])
+        torch.cuda.synchronize()
+        us = ev.elapsed_ms(e[0], e[1]) / reps * 1e3
+        ev.destroy(e)
+        del a
+        del scales
+        nbytes = 2 * up_bytes + E * 2 * 4 * 2
+        res[name] = {"us_per_call": round(us, 2), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1), "bytes": nbytes,
+                     "copies_rotated": copies}
+    return res
+
+
 def cpu_baseline(wl, seed, x, ids, wts, g13, g2, dense_expert, ntok):
     """The oracle (unchanged) on a bounded sample of the decode batch: ntok tokens and their experts."""
     import multiprocessing
@@ -370,6 +413,7 @@ def main():
                      "measured_peak": peaks["copy_GBps"], "frac_of_measured": round(achieved / peaks["copy_GBps"], 4)},
         "measured_peaks": peaks,
         "router": router_figures(moesq, torch, ev),
+        "fold_gate_up": fold_figures(moesq, torch, ev),
     }
     del layers[1:]
     torch.cuda.empty_cache()

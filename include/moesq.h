@@ -211,6 +211,21 @@ moesq_status moesq_prepare_weights(const moesq_weights *src /* host struct */, u
 moesq_status moesq_unprepare_weights(const uint8_t *tiled, int32_t E, int32_t N, int32_t K, uint8_t *packed,
                                      uint8_t *mask, uint8_t *scale, hipStream_t stream);
 
+/* Load-time fold of the gate/up global ratio into the block scales (model card
+ * "Qwen3.8-Flash-Next-P48NVFP4-MoESQ", the note under "Compression details", and model card
+ * "Qwen3-30B-A3B-P48NVFP4-MoESQ", the note after the evaluation table: gate and up carry separate
+ * globals, and the serving loader folds their ratio into the block scales so that one global serves
+ * both). In place on a fused gate|up linear in the pair-bitmask layout, before any re-tiling:
+ *   scale  [E][N][K/32] E4M3 bytes, rows [0, N/2) gate, [N/2, N) up. Each up byte s in 0x01..0x7E
+ *          becomes the E4M3 byte nearest to e4m3(s) * r (ties to even, saturating at 448),
+ *          r = fp32(global[e][1] / global[e][0]); 0x00 and bytes that are not finite non-negative
+ *          scales (0x7F and above) are left as they are. Gate rows are not touched.
+ *   global [E][2] fp32, gate then up, positive: global[e][1] is set to global[e][0] afterwards.
+ * N even, K % 32 == 0; E = 0 is a no-op. The result is lossy where a scale saturates or underflows.
+ * Errors: a negative status for bad sizes or a null pointer, nothing enqueued. */
+moesq_status moesq_fold_gate_up_globals(uint8_t *scale, float *global, int32_t E, int32_t N, int32_t K,
+                                        hipStream_t stream);
+
 /* Storage codec on whole tensors of `rows` rows of K (model card "Sparse storage layout": the encoding
  * is lossless).
  *   validate: *bad = number of chunk nibbles without exactly two bits set.

@@ -78,7 +78,8 @@ def fold_gate_up_globals(scale13, gw13):
     global serves both). Reading: the gate's global is the one kept for both halves (the one a loader
     without the fold would apply to both), and each up block scale s becomes the E4M3 code nearest to
     e4m3(s) * r (ties to even, saturating at 448), r = the fp32 quotient g_up / g_gate; a zero scale
-    stays zero. e4m3(s) has 4 significant bits and r 24, so the product is exact in float64.
+    stays zero, and a byte that is not a finite non-negative scale (0x7F and above) is left as it is.
+    e4m3(s) has 4 significant bits and r 24, so the product is exact in float64.
 
     scale13 u8 [2I, K/32] (gate rows, then up rows), gw13 [2] -> (scale u8 [2I, K/32], gw float32 [2]).
     """
@@ -90,9 +91,10 @@ def fold_gate_up_globals(scale13, gw13):
     with np.errstate(divide="ignore", invalid="ignore"):
         r = np.float64(np.float32(np.float64(gw13[1]) / np.float64(gw13[0])))
     up = scale13[N // 2:]
+    keep = (up == 0) | (up >= 0x7F)
     with np.errstate(invalid="ignore"):
-        v = nvfp4.e4m3fn_decode(up) * r
-    folded = np.where(up == 0, np.uint8(0), nvfp4.e4m3_rne_sat(np.where(up == 0, 0.0, v)))
+        v = nvfp4.e4m3fn_decode(np.where(keep, 0, up)) * r
+    folded = np.where(keep, up, nvfp4.e4m3_rne_sat(np.where(keep, 0.0, v)))
     out = scale13.copy()
     out[N // 2:] = folded
     return out, np.array([gw13[0], gw13[0]], dtype=np.float32)

@@ -38,7 +38,7 @@ EXPORTED_SYMBOLS = (
     "moesq_moe_ffn_workspace_size", "moesq_moe_ffn", "moesq_compress_weights", "moesq_validate_weights",
     "moesq_unpack_pair_bitmask", "moesq_pack_pair_bitmask", "moesq_set_stage_events", "moesq_tiled_bytes",
     "moesq_prepare_weights", "moesq_unprepare_weights", "moesq_permute_workspace_size", "moesq_probe_smfmac",
-    "moesq_route_topk",
+    "moesq_route_topk", "moesq_fold_gate_up_globals",
 )
 
 
@@ -89,6 +89,7 @@ def _declare(L: ctypes.CDLL) -> None:
         "moesq_probe_smfmac": (ctypes.c_int, [_I32, _I32, _P, ctypes.POINTER(_I64), _P]),
         "moesq_route_topk": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I32, _I32, _I32, _P, _P, _P]),
         "moesq_tiled_bytes": (_SZ, [_I32, _I32, _I32]),
+        "moesq_fold_gate_up_globals": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P]),
         "moesq_prepare_weights": (ctypes.c_int, [ctypes.POINTER(_CWeights), _P, _P]),
         "moesq_unprepare_weights": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _P, _P, _P]),
     }
@@ -211,7 +212,20 @@ def unprepare_weights(w: SparseWeights) -> SparseWeights:
     return SparseWeights(packed, mask, scale, w.global_scale)
 
 
-__all__ += ["LAYOUT_PAIR_BITMASK", "LAYOUT_TILED", "prepare_weights", "unprepare_weights"]
+def fold_gate_up_globals(w13: SparseWeights) -> SparseWeights:
+    """In place: fold each expert's up/gate global ratio into its up block scales and set the up
+    global to the gate's (pair-bitmask layout, G = 2). Returns ``w13``."""
+    if w13.layout != LAYOUT_PAIR_BITMASK or w13.G != 2:
+        raise MoesqError("fold_gate_up_globals needs a pair-bitmask gate|up linear with 2 globals per expert")
+    E, N, K = w13.E, w13.N, w13.K
+    if tuple(w13.scale.shape) != (E, N, K // 32):
+        raise MoesqError("scale shape does not match packed")
+    _check(lib().moesq_fold_gate_up_globals(_dev(w13.scale, "scale", torch.uint8),
+                                            _dev(w13.global_scale, "global_scale", torch.float32), E, N, K, _stream()))
+    return w13
+
+
+__all__ += ["LAYOUT_PAIR_BITMASK", "LAYOUT_TILED", "prepare_weights", "unprepare_weights", "fold_gate_up_globals"]
 
 
 def quantize_act(x: torch.Tensor, global_scale: torch.Tensor, src_row: Optional[torch.Tensor] = None,

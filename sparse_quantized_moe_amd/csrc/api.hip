@@ -327,6 +327,18 @@ moesq_status moesq_unprepare_weights(const uint8_t* tiled, int32_t E, int32_t N,
   return check_launch(stream, false);
 }
 
+moesq_status moesq_fold_gate_up_globals(uint8_t* scale, float* global, int32_t E, int32_t N, int32_t K,
+                                        hipStream_t stream) {
+  MOESQ_REQUIRE(E >= 0 && N >= 2 && N % 2 == 0 && K >= 32 && K % 32 == 0, MOESQ_ERR_INVALID,
+                "fold_gate_up_globals: E >= 0, N even, K a positive multiple of 32");
+  MOESQ_REQUIRE(E <= 65535, MOESQ_ERR_UNSUPPORTED, "fold_gate_up_globals: at most 65535 experts");
+  if (E == 0) return MOESQ_OK;
+  MOESQ_REQUIRE(scale && global, MOESQ_ERR_INVALID, "fold_gate_up_globals: null pointer");
+  MOESQ_REQUIRE(((uintptr_t)global & 3) == 0, MOESQ_ERR_INVALID, "fold_gate_up_globals: global must be 4-byte aligned");
+  moesq::launch_fold_gate_up(scale, global, E, N, K, stream);
+  return check_launch(stream, false);
+}
+
 moesq_status moesq_validate_weights(const uint8_t* mask, int64_t rows, int32_t K, int32_t* bad, hipStream_t stream) {
   MOESQ_REQUIRE(rows >= 0 && K > 0 && K % 32 == 0, MOESQ_ERR_INVALID, "validate_weights: K % 32 == 0");
   MOESQ_REQUIRE(bad && (rows == 0 || mask), MOESQ_ERR_INVALID, "validate_weights: null pointer");

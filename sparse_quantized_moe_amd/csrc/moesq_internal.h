@@ -23,6 +23,7 @@ void launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t stream);
 size_t tiled_bytes(int E, int N, int K);
 void launch_prepare(const uint8_t* packed, const uint8_t* mask, const uint8_t* scale, int E, int N, int K,
                     uint8_t* tiled, hipStream_t stream);
+void launch_fold_gate_up(uint8_t* scale, float* global, int E, int N, int K, hipStream_t stream);
 void launch_unprepare(const uint8_t* tiled, int E, int N, int K, uint8_t* packed, uint8_t* mask, uint8_t* scale,
                       hipStream_t stream);
 

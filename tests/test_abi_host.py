@@ -101,6 +101,11 @@ def test_argument_checks_return_status_without_launching():
     assert L.moesq_route_topk(P, 0, 4, 8, 2, 1, None, P, None) == INVALID
     assert b"null pointer" in L.moesq_last_error()
     assert L.moesq_route_topk(None, 0, 0, 8, 2, 1, None, None, None) == OK
+    # gate/up fold: odd N, K not a multiple of 32, null pointers; no experts is a no-op
+    assert L.moesq_fold_gate_up_globals(P, P, 4, 63, 256, None) == INVALID
+    assert L.moesq_fold_gate_up_globals(P, P, 4, 64, 48, None) == INVALID
+    assert L.moesq_fold_gate_up_globals(None, P, 4, 64, 256, None) == INVALID
+    assert L.moesq_fold_gate_up_globals(None, None, 0, 64, 256, None) == OK
     # compress and codec
     assert L.moesq_compress_weights(P, 4, 40, P, P, P, P, None) == INVALID
     assert L.moesq_validate_weights(P, 4, 40, P, None) == INVALID

@@ -208,14 +208,18 @@ def test_fold_gate_up_globals_vs_brute_force(gg, gu):
     I, G = 16, 8
     scale = rng.integers(0, 0x7F, size=(2 * I, G), dtype=np.uint8)
     scale[I, :4] = [0x00, 0x01, 0x7E, 0x08]                   # zero, smallest subnormal, 448, 2^-6
+    scale[I + 1, :3] = [0x7F, 0x80, 0xC5]                     # NaN and negative bytes: not scales
     gw = np.array([gg, gu], np.float32)
     out, gw2 = moe.fold_gate_up_globals(scale, gw)
     assert np.array_equal(out[:I], scale[:I])                 # gate rows untouched
     assert gw2.dtype == np.float32 and gw2[0] == gw[0] and gw2[1] == gw[0]
     r = _fp32_nearest(Fraction(float(gw[1])) / Fraction(float(gw[0])))
     for (i, j), s in np.ndenumerate(scale[I:]):
+        if s == 0 or s >= 0x7F:
+            assert out[I + i, j] == s                         # zero, and bytes that are not scales
+            continue
         v = Fraction(float(nvfp4.e4m3fn_decode(s))) * Fraction(float(r))
-        want = 0 if s == 0 else _nearest_e4m3_brute(v)
+        want = _nearest_e4m3_brute(v)
         assert out[I + i, j] == want, (i, j, int(s), float(v))
 
 
