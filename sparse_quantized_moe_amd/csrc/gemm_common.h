@@ -209,6 +209,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, const EpiScal
     const int I = N >> 1;
     const int hcol0 = nb * 128 + __builtin_amdgcn_readfirstlane(wv) * 32;
     const float g2 = es.h_global;
+    const float inv6g2 = scale_code_inv(g2);
 #pragma unroll
     for (int tt = 0; tt < TG; ++tt) {
       if (tt * 16 >= mrows) continue;
@@ -226,9 +227,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, const EpiScal
           h[half][r] = hv;
           amax = __builtin_fmaxf(amax, __builtin_fabsf(hv));
         }
-      amax = __builtin_fmaxf(amax, __shfl_xor(amax, 16));
-      amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32));
-      const int scb = scale_code(amax, g2);
+      amax = lane_max4(amax);
+      const int scb = scale_code(amax, g2, inv6g2);
       const float s = e4m3_value(scb);
       if (n < mrows) {
         const int64_t row = row0 + m0 + n;

@@ -35,34 +35,41 @@ __device__ __forceinline__ float e4m3_value(uint32_t b) {
 }
 
 // Nearest E4M3 byte of fp32 v >= 0 (may be off by one step near a midpoint; callers fix it exactly).
+// Selects only: the normal-range code (v = 1.f 2^e, 3 fraction bits rounded, a carry moving to the
+// next binade), the subnormal code (steps of 2^-9) below 2^-6, and 0x7E from 448 up (NaN included).
 __device__ __forceinline__ int e4m3_candidate(float v) {
-  if (!(v < 448.0f)) return 0x7E;
-  if (v < 0x1p-6f) return (int)__builtin_rintf(v * 512.0f);            // subnormal steps of 2^-9
   const uint32_t u = __float_as_uint(v);
-  const int e = (int)((u >> 23) & 255u) - 127;                         // v = 1.f * 2^e, e in [-6, 8]
+  const int e = (int)((u >> 23) & 255u) - 127;
   const float mant = __uint_as_float((u & 0x007FFFFFu) | 0x3F800000u); // [1, 2)
-  const int m = (int)__builtin_rintf((mant - 1.0f) * 8.0f);           // 0..8 (8 carries)
-  const int c = ((e + 7) << 3) + m;
-  return c < 0x7E ? c : 0x7E;
+  const int cn = ((e + 7) << 3) + (int)__builtin_rintf((mant - 1.0f) * 8.0f);
+  const int cs = (int)__builtin_rintf(__builtin_fminf(v, 1.0f) * 512.0f);
+  const int c = v < 0x1p-6f ? cs : (cn < 0x7E ? cn : 0x7E);
+  return v < 448.0f ? c : 0x7E;
+}
+
+// Midpoint of E4M3 bytes c and c + 1 (0 <= c < 0x7E), exact in fp32: a normal byte's value plus half
+// its step is the same bits with mantissa bit 19 set (the next byte, also in the next binade, is one
+// full step up); below 2^-6 the step is 2^-9 and the midpoint (2c + 1) 2^-10.
+__device__ __forceinline__ float e4m3_mid_up(uint32_t c) {
+  const float normal = __uint_as_float((((c >> 3) + 120u) << 23) | ((c & 7u) << 20) | (1u << 19));
+  const float sub = (float)(2u * c + 1u) * 0x1p-10f;
+  return c >= 8u ? normal : sub;
 }
 
 // E4M3 byte of the exact quotient amax / (6 g): round to nearest, ties to even, saturating at 448.
-// amax >= 0, g > 0. The fp32 candidate is within one step; the two neighbouring midpoints m are
-// tested exactly with sign(fma(-(6m), g, amax)) (6m has <= 7 significant bits).
-__device__ __forceinline__ int scale_code(float amax, float g) {
-  int c = e4m3_candidate(amax / (6.0f * g));
-  if (c < 0x7E) {
-    const float mhi = 0.5f * (e4m3_value(c) + e4m3_value(c + 1));
-    const float dhi = __builtin_fmaf(-6.0f * mhi, g, amax);
-    if (dhi > 0.0f || (dhi == 0.0f && (c & 1))) return c + 1;
-  }
-  if (c > 0) {
-    const float mlo = 0.5f * (e4m3_value(c - 1) + e4m3_value(c));
-    const float dlo = __builtin_fmaf(-6.0f * mlo, g, amax);
-    if (dlo < 0.0f || (dlo == 0.0f && (c & 1))) return c - 1;
-  }
-  return c;
+// amax >= 0, g > 0, inv6g ~ 1 / (6 g) (a few ulps off is fine). The candidate from amax * inv6g is
+// within one step of the answer; the midpoints m with its two neighbours are tested exactly with
+// sign(fma(-(6m), g, amax)) (6m has <= 7 significant bits), with no branch.
+__device__ __forceinline__ int scale_code(float amax, float g, float inv6g) {
+  const int c = e4m3_candidate(amax * inv6g);
+  const float dhi = __builtin_fmaf(-6.0f * e4m3_mid_up((uint32_t)c), g, amax);
+  const float dlo = __builtin_fmaf(-6.0f * e4m3_mid_up((uint32_t)(c - 1)), g, amax);
+  const bool up = c < 0x7E && (dhi > 0.0f || (dhi == 0.0f && (c & 1)));
+  const bool down = c > 0 && (dlo < 0.0f || (dlo == 0.0f && (c & 1)));
+  return c + (up ? 1 : 0) - (down ? 1 : 0);
 }
+__device__ __forceinline__ float scale_code_inv(float g) { return __builtin_amdgcn_rcpf(6.0f * g); }
+__device__ __forceinline__ int scale_code(float amax, float g) { return scale_code(amax, g, scale_code_inv(g)); }
 
 // E2M1 magnitude code (0..7) of the exact quotient ax / (s g): nearest, ties to even, saturating at 6.
 // Boundaries 0.25 .75 1.25 1.75 2.5 3.5 5; a tie goes to the even code (strict '>' where the lower
@@ -122,12 +129,13 @@ template <int N>
 __device__ __forceinline__ uint32_t nvfp4_codes(const float* x, float s, float g, Nvfp4Recip rc) {
   static_assert(N % 2 == 0 && N <= 8, "whole bytes of one word");
   float r[N];
-  bool near = rc.exact;
+  uint32_t nearest = 0xFFFFFFFFu;   // 0 iff some r is within 16 ulps of a boundary (nvfp4_near)
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     r[i] = x[i] * rc.inv;
-    near = near || nvfp4_near(r[i]);
+    nearest = __builtin_elementwise_min(nearest, (__float_as_uint(r[i]) + 16u) & 0x1FFFE0u);
   }
+  const bool near = rc.exact || nearest == 0u;
   // the byte selector of the conversion has to be a constant
   uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, r[0], r[1], 1.0f, 0);
   if constexpr (N >= 4) w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, r[2], r[3], 1.0f, 1);
@@ -135,6 +143,17 @@ __device__ __forceinline__ uint32_t nvfp4_codes(const float* x, float s, float g
   if constexpr (N >= 8) w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, r[6], r[7], 1.0f, 3);
   if (near) w = nvfp4_codes_exact<N>(x, s, g);
   return w;
+}
+
+// Maximum of v over the four lanes l, l ^ 16, l ^ 32, l ^ 48 of a wave, in every one of them: a swap
+// of odd and even 16-lane rows, then of the two 32-lane halves, each followed by a max.
+__device__ __forceinline__ float lane_max4(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float m = __builtin_fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t mu = __float_as_uint(m);
+  const auto b = __builtin_amdgcn_permlane32_swap(mu, mu, false, false);
+  return __builtin_fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
