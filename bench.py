@@ -166,9 +166,9 @@ def measured_peaks(moesq, torch, ev):
     del src, dst
     blocks = 2 * torch.cuda.get_device_properties(0).multi_processor_count
     sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
-    moesq.probe_smfmac(blocks, 256, sink)
+    moesq.probe_smfmac(blocks, 64, sink)
     ev.record(e[0])
-    insts = moesq.probe_smfmac(blocks, 4096, sink)
+    insts = moesq.probe_smfmac(blocks, 1024, sink)
     ev.record(e[1])
     torch.cuda.synchronize()
     tf = insts * 16384 / (ev.elapsed_ms(e[0], e[1]) * 1e-3) / 1e12

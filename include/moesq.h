@@ -188,8 +188,9 @@ moesq_status moesq_set_stage_events(hipEvent_t *events /* host */, int32_t n);
 
 /* Measurement aid: a throughput probe of v_smfmac_f32_16x16x64_f16, the instruction the grouped GEMMs
  * are built on, so rooflines can be quoted against the rate this GPU sustains besides the published
- * peak. Launches `blocks` workgroups of 4 waves, each wave issuing iters x 8 independent instructions
- * (16 x 16 outputs, 64 dense K: 16384 multiply-adds on the kept half); time it with events on
+ * peak. Launches `blocks` workgroups of 4 waves, each wave issuing iters x 32 independent instructions
+ * (4 sparse x 8 dense operands, the GEMMs' pattern; each 16 x 16 outputs over 64 dense K: 16384
+ * multiply-adds on the kept half); time it with events on
  * `stream`. sink: blocks * 256 floats (device, written). *n_insts (host): instructions issued.
  * blocks >= 1, iters >= 1. */
 moesq_status moesq_probe_smfmac(int32_t blocks, int32_t iters, float *sink, int64_t *n_insts /* host */,

@@ -64,9 +64,10 @@ __device__ __forceinline__ int scale_code(float amax, float g, float inv6g) {
   const int c = e4m3_candidate(amax * inv6g);
   const float dhi = __builtin_fmaf(-6.0f * e4m3_mid_up((uint32_t)c), g, amax);
   const float dlo = __builtin_fmaf(-6.0f * e4m3_mid_up((uint32_t)(c - 1)), g, amax);
-  const bool up = c < 0x7E && (dhi > 0.0f || (dhi == 0.0f && (c & 1)));
-  const bool down = c > 0 && (dlo < 0.0f || (dlo == 0.0f && (c & 1)));
-  return c + (up ? 1 : 0) - (down ? 1 : 0);
+  const bool odd = (c & 1) != 0;
+  const bool up = (c < 0x7E) & ((dhi > 0.0f) | ((dhi == 0.0f) & odd));
+  const bool down = (c > 0) & ((dlo < 0.0f) | ((dlo == 0.0f) & odd));
+  return c + (int)up - (int)down;
 }
 __device__ __forceinline__ float scale_code_inv(float g) { return __builtin_amdgcn_rcpf(6.0f * g); }
 __device__ __forceinline__ int scale_code(float amax, float g) { return scale_code(amax, g, scale_code_inv(g)); }
@@ -145,15 +146,15 @@ __device__ __forceinline__ uint32_t nvfp4_codes(const float* x, float s, float g
   return w;
 }
 
-// Maximum of v over the four lanes l, l ^ 16, l ^ 32, l ^ 48 of a wave, in every one of them: a swap
-// of odd and even 16-lane rows, then of the two 32-lane halves, each followed by a max.
+// Maximum of v >= 0 over the four lanes l, l ^ 16, l ^ 32, l ^ 48 of a wave, in every one of them: a
+// swap of odd and even 16-lane rows, then of the two 32-lane halves, each followed by a max (on the
+// bit patterns, which order non-negative floats as their values).
 __device__ __forceinline__ float lane_max4(float v) {
   const uint32_t u = __float_as_uint(v);
   const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  const float m = __builtin_fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const uint32_t mu = __float_as_uint(m);
-  const auto b = __builtin_amdgcn_permlane32_swap(mu, mu, false, false);
-  return __builtin_fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  const uint32_t m = a[0] > a[1] ? a[0] : a[1];
+  const auto b = __builtin_amdgcn_permlane32_swap(m, m, false, false);
+  return __uint_as_float(b[0] > b[1] ? b[0] : b[1]);
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }

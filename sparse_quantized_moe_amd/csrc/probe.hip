@@ -1,38 +1,52 @@
 // Throughput probe of the instruction the grouped GEMMs are built on, v_smfmac_f32_16x16x64_f16, so a
 // roofline can be quoted against the rate this GPU sustains as well as against the published peak.
-// Each wave keeps 8 independent accumulator chains (enough to cover the instruction's latency) and
-// stores its accumulators at the end, so nothing is folded away.
+// Each wave runs the GEMMs' own issue pattern: 4 sparse operands x 8 dense operands, 32 independent
+// accumulators (the most a wave of the prefill GEMM keeps), and stores its accumulators at the end, so
+// nothing is folded away. Two workgroups per CU give every SIMD two waves, as in the GEMMs.
 #include "moesq_device.h"
 #include "moesq_internal.h"
 
 namespace moesq {
 
-constexpr int kProbeChains = 8;
+constexpr int kProbeA = 4, kProbeB = 8;
 
 __global__ __launch_bounds__(256) void k_probe_smfmac(float* __restrict__ sink, int iters) {
-  f16x8 a;
-  f16x16 b;
+  f16x8 a[kProbeA];
+  f16x16 b[kProbeB];
+  int idx[kProbeA];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) a[i] = (f16)(0.001f * (float)(threadIdx.x + i));
+  for (int r = 0; r < kProbeA; ++r) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) b[i] = (f16)(0.002f * (float)((int)threadIdx.x - i));
-  f32x4 acc[kProbeChains];
+    for (int i = 0; i < 8; ++i) a[r][i] = (f16)(0.001f * (float)(threadIdx.x + i + r));
+    idx[r] = 0x4E4E4E4E ^ r;
+  }
 #pragma unroll
-  for (int j = 0; j < kProbeChains; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < kProbeB; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) b[t][i] = (f16)(0.002f * (float)((int)threadIdx.x - i - t));
+  f32x4 acc[kProbeA][kProbeB];
+#pragma unroll
+  for (int r = 0; r < kProbeA; ++r)
+#pragma unroll
+    for (int t = 0; t < kProbeB; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
-    for (int j = 0; j < kProbeChains; ++j)
-      acc[j] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(a, b, acc[j], 0x4444, 0, 0);
+    for (int t = 0; t < kProbeB; ++t)
+#pragma unroll
+      for (int r = 0; r < kProbeA; ++r)
+        acc[r][t] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(a[r], b[t], acc[r][t], idx[r], 0, 0);
   }
   float s = 0.f;
 #pragma unroll
-  for (int j = 0; j < kProbeChains; ++j) s += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+  for (int r = 0; r < kProbeA; ++r)
+#pragma unroll
+    for (int t = 0; t < kProbeB; ++t) s += acc[r][t][0] + acc[r][t][1] + acc[r][t][2] + acc[r][t][3];
   sink[(int64_t)blockIdx.x * 256 + threadIdx.x] = s;
 }
 
 int64_t launch_probe_smfmac(int blocks, int iters, float* sink, hipStream_t stream) {
   k_probe_smfmac<<<blocks, 256, 0, stream>>>(sink, iters);
-  return (int64_t)blocks * 4 * iters * kProbeChains;
+  return (int64_t)blocks * 4 * iters * kProbeA * kProbeB;
 }
 
 }  // namespace moesq

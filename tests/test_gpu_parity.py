@@ -444,9 +444,9 @@ def test_moe_ffn_fused_matches_separate_launches(case):
 
 
 def test_probe_smfmac_counts_and_writes():
-    """The MFMA throughput probe issues blocks x 4 waves x iters x 8 instructions and writes its sink."""
+    """The MFMA throughput probe issues blocks x 4 waves x iters x 32 instructions and writes its sink."""
     sink = torch.full((4 * 256,), float("nan"), dtype=torch.float32, device=DEV)
     n = moesq.probe_smfmac(4, 16, sink)
     torch.cuda.synchronize()
-    assert n == 4 * 4 * 16 * 8
+    assert n == 4 * 4 * 16 * 32
     assert torch.isfinite(sink).all()
