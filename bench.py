@@ -115,16 +115,18 @@ def touched_bytes(ids, E, H, I):
 def run_steps(moesq, torch, ev, x, ids_t, wts_t, layers, g13_t, g2_t, out, ws, warmup, steps, staged=False, flags=0):
     """Untimed warmup, then exactly ``steps`` timed calls bracketed by synchronizations.
 
-    Returns (wall seconds, stage times [steps][stages] in ms or None, GPU ms per step). Without
+    Returns (wall seconds, stage times [steps][stages + 1] in ms or None, GPU ms per step). Without
     ``staged`` the calls run back to back with HIP events only around the whole region; with it every
-    call records events between its stages (on the library's stream), which adds a little time."""
+    call records events between its stages (on the library's stream), which adds a little time, and
+    the last column is the gate/up GEMM kernel alone (or the one-launch kernel), from the two events
+    that kernel's dispatch records at its own start and end."""
     nl = len(layers)
     ns = len(moesq.FFN_STAGES)
     for i in range(warmup):
         w13, w2 = layers[i % nl]
         moesq.moe_ffn(x, ids_t, wts_t, w13, w2, g13_t, g2_t, out=out, workspace=ws, flags=flags)
     torch.cuda.synchronize()
-    evs = [ev.create(ns + 1) for _ in range(steps)] if staged else []
+    evs = [ev.create(ns + 3) for _ in range(steps)] if staged else []
     region = ev.create(2)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -141,7 +143,8 @@ def run_steps(moesq, torch, ev, x, ids_t, wts_t, layers, g13_t, g2_t, out, ws, w
     stages = None
     if staged:
         moesq.set_stage_events(None)
-        stages = np.array([[ev.elapsed_ms(e[j], e[j + 1]) for j in range(ns)] for e in evs])
+        stages = np.array([[ev.elapsed_ms(e[j], e[j + 1]) for j in range(ns)] + [ev.elapsed_ms(e[ns + 1], e[ns + 2])]
+                           for e in evs])
     for e in evs + [region]:
         ev.destroy(e)
     return wall, stages, gpu_ms
@@ -355,7 +358,8 @@ def main():
                                   args.warmup, args.steps, staged=True, flags=DEFAULT_FLAGS)
     st_mean = stages.mean(axis=0)
     log("decode stage us (mean): " + ", ".join(f"{n}={v * 1e3:.1f}" for n, v in zip(moesq.FFN_STAGES, st_mean))
-        + f"; {st_gpu * 1e3:.1f} us/step with stage events" + (" (one fused launch: all in the first)" if fused else ""))
+        + f"; {st_gpu * 1e3:.1f} us/step with stage events" + (" (one fused launch: all in the first)" if fused else "")
+        + f"; timed kernel alone {st_mean[-1] * 1e3:.1f} us")
     # the other path on the same batch, for comparison (separate launches vs the one-launch kernel)
     alt = None
     alt_flags = moesq.FLAG_UNFUSED if fused else moesq.FLAG_FUSED
@@ -379,14 +383,14 @@ def main():
         # experts + the tokens in (bf16) + router ids and weights + the output (fp32)
         kname = "k_ffn_fused (route, gate/up, down, combine in one launch)"
         kbytes = wbytes + wl.T * wl.H * 2 + P * 8 + wl.T * wl.H * 4
-        k_ms = float(st_mean.sum())
+        k_ms = float(st_mean[-1])          # the kernel's own start/end events
         tname, tsrc = "traffic_ffn_fused_qwen3_30b_decode.json", ("ffn_fused.hip", "gemm_common.h", "moesq_device.h")
     else:
         # dominant kernel: gate/up GEMM; algorithmic bytes = W13 stored bytes of touched experts + its
         # activation input (codes + scales) + its output (down-input codes + scales)
         kname = "k_gemm_decode_stream<gate_up>"
         kbytes = n_touched * (2 * wl.I * wl.H * 11 // 32 + 8) + P * (wl.H // 2 + wl.H // 32) + P * (wl.I // 2 + wl.I // 32)
-        k_ms = float(st_mean[moesq.FFN_STAGES.index("gemm_gate_up")])
+        k_ms = float(st_mean[-1])          # the kernel's own start/end events
         tname, tsrc = "traffic_gemm_gate_up_qwen3_30b_decode.json", ("gemm.hip", "gemm_common.h", "moesq_device.h")
     achieved = kbytes / (k_ms * 1e-3) / 1e9
     traffic = None
@@ -434,7 +438,7 @@ def main():
         PP = int((pids >= 0).sum())
         eff = 6.0 * PP * pw.H * pw.I / (pwall / psteps) / 1e12
         pst_mean = pst.mean(axis=0)
-        g_ms = float(pst_mean[moesq.FFN_STAGES.index("gemm_gate_up")])
+        g_ms = float(pst_mean[-1])         # the gate/up kernel's own start/end events
         alg_flops = 2.0 * PP * (2 * pw.I) * pw.H / 2          # multiply-adds on the kept half of W13
         ach = alg_flops / (g_ms * 1e-3) / 1e12
         log("prefill stage ms (mean): " + ", ".join(f"{n}={v:.3f}ms" for n, v in zip(moesq.FFN_STAGES, pst_mean)))

@@ -9,6 +9,15 @@ namespace {
 
 thread_local std::string g_last_error;
 thread_local hipEvent_t* g_stage_events = nullptr;
+thread_local int g_stage_n = 0;
+
+// events[5], events[6] (when given) are recorded by the timed kernel itself, at its start and end
+struct TimedKernel {
+  explicit TimedKernel() {
+    if (g_stage_events && g_stage_n >= 7) moesq::kernel_events() = {g_stage_events[5], g_stage_events[6]};
+  }
+  ~TimedKernel() { moesq::kernel_events() = {}; }
+};
 
 void stage_event(int i, hipStream_t stream) {
   if (g_stage_events) (void)hipEventRecord(g_stage_events[i], stream);
@@ -89,6 +98,7 @@ const char* moesq_last_error(void) { return g_last_error.c_str(); }
 moesq_status moesq_set_stage_events(hipEvent_t* events, int32_t n) {
   MOESQ_REQUIRE(!events || n >= 5, MOESQ_ERR_INVALID, "set_stage_events: need at least 5 events");
   g_stage_events = events;
+  g_stage_n = events ? n : 0;
   return MOESQ_OK;
 }
 
@@ -260,7 +270,11 @@ moesq_status moesq_moe_ffn(const void* x, int64_t T, int32_t H, const int32_t* t
     f.counts = counts; f.offsets = offsets; f.sorted = sorted; f.inv = inv; f.status = status;
     f.a13c = a13c; f.a13s = a13s; f.a2c = a2c; f.a2s = a2s; f.D = drows; f.out = out; f.sync = ws + L.sync;
     stage_event(0, stream);
-    const hipError_t err = moesq::launch_ffn_fused(f, stream);
+    hipError_t err;
+    {
+      const TimedKernel timed;
+      err = moesq::launch_ffn_fused(f, stream);
+    }
     for (int i = 1; i <= 4; ++i) stage_event(i, stream);
     if (err != hipSuccess) return fail(MOESQ_ERR_HIP, "moe_ffn: fused launch: %s", hipGetErrorString(err));
     return check_launch(stream, (flags & MOESQ_FLAG_SYNC_CHECK) != 0);
@@ -276,7 +290,10 @@ moesq_status moesq_moe_ffn(const void* x, int64_t T, int32_t H, const int32_t* t
   g.a_codes = a13c; g.a_scales = a13s; g.a_global = a13_global; g.offsets = offsets; g.tile_offsets = tile_offsets;
   g.a_rows = sorted; g.rows = P; g.w_packed = w13->packed; g.w_mask = w13->mask; g.w_scale = w13->scale; g.w_global = w13->global;
   g.E = E; g.N = w13->N; g.K = H; g.G = 2; g.layout = w13->layout; g.h_codes = a2c; g.h_scales = a2s; g.h_global = a2_global;
-  moesq::launch_grouped_gemm(g, moesq::kEpiGateUp, tactic, stream);
+  {
+    const TimedKernel timed;
+    moesq::launch_grouped_gemm(g, moesq::kEpiGateUp, tactic, stream);
+  }
   stage_event(2, stream);
   moesq::GemmParams d{};
   d.a_codes = a2c; d.a_scales = a2s; d.a_global = a2_global; d.offsets = offsets; d.tile_offsets = tile_offsets;

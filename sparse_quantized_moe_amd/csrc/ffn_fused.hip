@@ -603,7 +603,7 @@ hipError_t launch_ffn_fused(const FusedLaunch& f, hipStream_t stream) {
   // runtime reports (fused_applicable). A cooperative launch, which would also check this, cost
   // about 19 us more per call on MI355X. Should other work hold CUs, the barrier waits end with
   // status -1 instead of hanging.
-  k_ffn_fused<<<dim3((unsigned)(a.E * a.parts)), dim3(kFzThreads), fused_lds_bytes(a.H, a.I, a.T * a.k), stream>>>(a);
+  launch_kernel(k_ffn_fused, dim3((unsigned)(a.E * a.parts)), dim3(kFzThreads), fused_lds_bytes(a.H, a.I, a.T * a.k), stream, a);
   return hipGetLastError();
 }
 

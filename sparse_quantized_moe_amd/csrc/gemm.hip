@@ -646,6 +646,11 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_prefill(GemmParams p) {
   gemm_epilogue<EPI, TG>(p, es, acc, row0, m0, mrows, nb, wv, wrow, s_rw, lane);
 }
 
+KernelEvents& kernel_events() {
+  static thread_local KernelEvents ev;
+  return ev;
+}
+
 int tactic_rows_per_mblock(int tactic) { return tactic == kTacticPrefill ? kPreBMT : kDecTG * 16; }
 
 size_t gemm_lds_bytes(int tactic, int K) {
@@ -679,7 +684,8 @@ static void launch_decode(const GemmParams& p, hipStream_t stream) {
       set_lds_attr(&k_gemm_decode_stream<EPI, RT, DEPTH>, stream_lds_bytes(kStreamMaxK));
       const int waves = (p.N >> 1) / 32;
       const int groups = (waves + kStreamWaves - 1) / kStreamWaves;
-      k_gemm_decode_stream<EPI, RT, DEPTH><<<dim3((unsigned)p.E, (unsigned)groups), kStreamThreads, lds, stream>>>(p);
+      launch_kernel(k_gemm_decode_stream<EPI, RT, DEPTH>, dim3((unsigned)p.E, (unsigned)groups), dim3(kStreamThreads), lds,
+                    stream, p);
       return;
     }
   }
@@ -689,14 +695,14 @@ static void launch_decode(const GemmParams& p, hipStream_t stream) {
       const size_t lds = DecGeom<DEPTH>::lds;
       set_lds_attr(&k_gemm_decode_nloop<EPI, LAYOUT, RT, DEPTH>, lds);
       const int ny = (nblocks + kNloopBlocks - 1) / kNloopBlocks;
-      k_gemm_decode_nloop<EPI, LAYOUT, RT, DEPTH>
-          <<<dim3((unsigned)p.E, (unsigned)ny), kGemmThreads, lds, stream>>>(p, nblocks);
+      launch_kernel(k_gemm_decode_nloop<EPI, LAYOUT, RT, DEPTH>, dim3((unsigned)p.E, (unsigned)ny), dim3(kGemmThreads), lds,
+                    stream, p, nblocks);
       return;
     }
   }
   const size_t lds = DecGeom<DEPTH>::lds;
   set_lds_attr(&k_gemm_decode<EPI, LAYOUT, RT>, lds);
-  k_gemm_decode<EPI, LAYOUT, RT><<<dim3((unsigned)p.E, (unsigned)nblocks), kGemmThreads, lds, stream>>>(p);
+  launch_kernel(k_gemm_decode<EPI, LAYOUT, RT>, dim3((unsigned)p.E, (unsigned)nblocks), dim3(kGemmThreads), lds, stream, p);
 }
 
 template <int EPI, int LAYOUT>
@@ -708,7 +714,7 @@ static void launch_prefill(const GemmParams& p, hipStream_t stream) {
   const int64_t mblocks = (p.rows + kPreBMT - 1) / kPreBMT + p.E;
   const int nblocks = EPI == kEpiGateUp ? ((p.N >> 1) + 127) / 128 : (p.N + 255) / 256;
   const int64_t grid = ((mblocks * nblocks + kXcds - 1) / kXcds) * kXcds;
-  k_gemm_prefill<EPI, LAYOUT><<<dim3((unsigned)grid), kGemmThreads, lds, stream>>>(p);
+  launch_kernel(k_gemm_prefill<EPI, LAYOUT>, dim3((unsigned)grid), dim3(kGemmThreads), lds, stream, p);
 }
 
 template <int EPI>

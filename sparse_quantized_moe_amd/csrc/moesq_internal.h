@@ -1,6 +1,7 @@
 // Host-side launchers shared between the kernel files and the C ABI layer.
 #pragma once
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 namespace moesq {
@@ -116,5 +117,21 @@ int64_t launch_probe_smfmac(int blocks, int iters, float* sink, hipStream_t stre
 
 // out[t][:] = sum_j D[inv[t*k + j]][:] (rows with inv < 0 skipped), in j order.
 void launch_combine(const float* D, const int* inv, int64_t T, int k, int H, float* out, hipStream_t stream);
+
+// Optional start/stop events that the next GEMM or one-launch FFN kernel records itself, at its own
+// start and end (hipExtLaunchKernelGGL), for timing that kernel alone; null: plain launches.
+struct KernelEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+KernelEvents& kernel_events();   // this host thread's
+
+template <typename F, typename... Args>
+inline void launch_kernel(F kernel, dim3 grid, dim3 block, size_t lds, hipStream_t stream, Args... args) {
+  const KernelEvents ev = kernel_events();
+  if (ev.start)
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, stream, ev.start, ev.stop, 0u, args...);
+  else
+    kernel<<<grid, block, lds, stream>>>(args...);
+}
 
 }  // namespace moesq
