@@ -115,18 +115,19 @@ def touched_bytes(ids, E, H, I):
 def run_steps(moesq, torch, ev, x, ids_t, wts_t, layers, g13_t, g2_t, out, ws, warmup, steps, staged=False, flags=0):
     """Untimed warmup, then exactly ``steps`` timed calls bracketed by synchronizations.
 
-    Returns (wall seconds, stage times [steps][stages + 1] in ms or None, GPU ms per step). Without
+    Returns (wall seconds, stage times [steps][2 * stages] in ms or None, GPU ms per step). Without
     ``staged`` the calls run back to back with HIP events only around the whole region; with it every
-    call records events between its stages (on the library's stream), which adds a little time, and
-    the last column is the gate/up GEMM kernel alone (or the one-launch kernel), from the two events
-    that kernel's dispatch records at its own start and end."""
+    call records events between its stages (on the library's stream), which adds a little time: the
+    first ``stages`` columns are those intervals (launch gaps included), the next ``stages`` the
+    stages' kernels alone, from the events their own dispatches record (on the one-launch path the
+    single kernel is the first of these and the others are empty)."""
     nl = len(layers)
     ns = len(moesq.FFN_STAGES)
     for i in range(warmup):
         w13, w2 = layers[i % nl]
         moesq.moe_ffn(x, ids_t, wts_t, w13, w2, g13_t, g2_t, out=out, workspace=ws, flags=flags)
     torch.cuda.synchronize()
-    evs = [ev.create(ns + 3) for _ in range(steps)] if staged else []
+    evs = [ev.create(3 * ns + 1) for _ in range(steps)] if staged else []
     region = ev.create(2)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -143,8 +144,8 @@ def run_steps(moesq, torch, ev, x, ids_t, wts_t, layers, g13_t, g2_t, out, ws, w
     stages = None
     if staged:
         moesq.set_stage_events(None)
-        stages = np.array([[ev.elapsed_ms(e[j], e[j + 1]) for j in range(ns)] + [ev.elapsed_ms(e[ns + 1], e[ns + 2])]
-                           for e in evs])
+        stages = np.array([[ev.elapsed_ms(e[j], e[j + 1]) for j in range(ns)] +
+                           [ev.elapsed_ms(e[ns + 1 + 2 * j], e[ns + 2 + 2 * j]) for j in range(ns)] for e in evs])
     for e in evs + [region]:
         ev.destroy(e)
     return wall, stages, gpu_ms
@@ -254,6 +255,16 @@ def fold_figures(moesq, torch, ev, reps=20):
     return res
 
 
+def side_passes(wl, P, route_ms, combine_ms):
+    """The two HBM-bound passes around the GEMMs, from their kernels' own start/end events: routing
+    (router ids in; x in, bf16; activation codes and scales out; sorted and inv out) and the top-k
+    combine (the P fp32 down rows and inv in, the fp32 output out)."""
+    rb = P * 4 + wl.T * wl.H * 2 + P * (wl.H // 2 + wl.H // 32) + 2 * P * 4
+    cb = P * wl.H * 4 + P * 4 + wl.T * wl.H * 4
+    return {"route": {"us": round(route_ms * 1e3, 2), "bytes": rb, "GBps": round(rb / (route_ms * 1e-3) / 1e9, 1)},
+            "combine": {"us": round(combine_ms * 1e3, 2), "bytes": cb, "GBps": round(cb / (combine_ms * 1e-3) / 1e9, 1)}}
+
+
 def cpu_baseline(wl, seed, x, ids, wts, g13, g2, dense_expert, ntok):
     """The oracle (unchanged) on a bounded sample of the decode batch: ntok tokens and their experts."""
     import multiprocessing
@@ -359,7 +370,7 @@ def main():
     st_mean = stages.mean(axis=0)
     log("decode stage us (mean): " + ", ".join(f"{n}={v * 1e3:.1f}" for n, v in zip(moesq.FFN_STAGES, st_mean))
         + f"; {st_gpu * 1e3:.1f} us/step with stage events" + (" (one fused launch: all in the first)" if fused else "")
-        + f"; timed kernel alone {st_mean[-1] * 1e3:.1f} us")
+        + "; kernels alone " + ", ".join(f"{n}={v * 1e3:.1f}" for n, v in zip(moesq.FFN_STAGES, st_mean[len(moesq.FFN_STAGES):])))
     # the other path on the same batch, for comparison (separate launches vs the one-launch kernel)
     alt = None
     alt_flags = moesq.FLAG_UNFUSED if fused else moesq.FLAG_FUSED
@@ -383,14 +394,14 @@ def main():
         # experts + the tokens in (bf16) + router ids and weights + the output (fp32)
         kname = "k_ffn_fused (route, gate/up, down, combine in one launch)"
         kbytes = wbytes + wl.T * wl.H * 2 + P * 8 + wl.T * wl.H * 4
-        k_ms = float(st_mean[-1])          # the kernel's own start/end events
+        k_ms = float(st_mean[len(moesq.FFN_STAGES)])       # the one kernel, its own start/end events
         tname, tsrc = "traffic_ffn_fused_qwen3_30b_decode.json", ("ffn_fused.hip", "gemm_common.h", "moesq_device.h")
     else:
         # dominant kernel: gate/up GEMM; algorithmic bytes = W13 stored bytes of touched experts + its
         # activation input (codes + scales) + its output (down-input codes + scales)
         kname = "k_gemm_decode_stream<gate_up>"
         kbytes = n_touched * (2 * wl.I * wl.H * 11 // 32 + 8) + P * (wl.H // 2 + wl.H // 32) + P * (wl.I // 2 + wl.I // 32)
-        k_ms = float(st_mean[-1])          # the kernel's own start/end events
+        k_ms = float(st_mean[len(moesq.FFN_STAGES) + 1])   # the gate/up kernel, its own start/end events
         tname, tsrc = "traffic_gemm_gate_up_qwen3_30b_decode.json", ("gemm.hip", "gemm_common.h", "moesq_device.h")
     achieved = kbytes / (k_ms * 1e-3) / 1e9
     traffic = None
@@ -409,6 +420,7 @@ def main():
                    "weight_copies_rotated": args.copies, "warm_cache_GBps": round(warm, 2),
                    "gpu_us_per_step": round(gpu_ms * 1e3, 2), "fused_launch": fused,
                    "stage_us": {n: round(float(v) * 1e3, 2) for n, v in zip(moesq.FFN_STAGES, st_mean)},
+                   "kernel_us": {n: round(float(v) * 1e3, 2) for n, v in zip(moesq.FFN_STAGES, st_mean[len(moesq.FFN_STAGES):])},
                    "other_path": alt},
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -416,6 +428,8 @@ def main():
                      "avg_launch_us": round(k_ms * 1e3, 2),
                      "measured_peak": peaks["copy_GBps"], "frac_of_measured": round(achieved / peaks["copy_GBps"], 4)},
         "measured_peaks": peaks,
+        "side_passes": None if fused else side_passes(wl, P, float(st_mean[len(moesq.FFN_STAGES)]),
+                                                      float(st_mean[len(moesq.FFN_STAGES) + 3])),
         "router": router_figures(moesq, torch, ev),
         "fold_gate_up": fold_figures(moesq, torch, ev),
     }
@@ -438,15 +452,19 @@ def main():
         PP = int((pids >= 0).sum())
         eff = 6.0 * PP * pw.H * pw.I / (pwall / psteps) / 1e12
         pst_mean = pst.mean(axis=0)
-        g_ms = float(pst_mean[-1])         # the gate/up kernel's own start/end events
+        g_ms = float(pst_mean[len(moesq.FFN_STAGES) + 1])  # the gate/up kernel, its own start/end events
         alg_flops = 2.0 * PP * (2 * pw.I) * pw.H / 2          # multiply-adds on the kept half of W13
         ach = alg_flops / (g_ms * 1e-3) / 1e12
-        log("prefill stage ms (mean): " + ", ".join(f"{n}={v:.3f}ms" for n, v in zip(moesq.FFN_STAGES, pst_mean)))
+        log("prefill stage ms (mean): " + ", ".join(f"{n}={v:.3f}ms" for n, v in zip(moesq.FFN_STAGES, pst_mean))
+            + "; kernels alone " + ", ".join(f"{n}={v:.3f}ms" for n, v in zip(moesq.FFN_STAGES, pst_mean[len(moesq.FFN_STAGES):])))
         log(f"prefill: {pwall / psteps * 1e3:.3f} ms/step, {eff:.1f} effective dense TFLOP/s")
         result["prefill"] = {
             "workload": pw.name, "tokens": pw.T, "value": round(eff, 2), "unit": "effective dense TFLOP/s",
             "ms_per_step": round(pwall / psteps * 1e3, 4), "steps": psteps,
             "stage_ms": {n: round(float(v), 4) for n, v in zip(moesq.FFN_STAGES, pst_mean)},
+            "kernel_ms": {n: round(float(v), 4) for n, v in zip(moesq.FFN_STAGES, pst_mean[len(moesq.FFN_STAGES):])},
+            "side_passes": side_passes(pw, PP, float(pst_mean[len(moesq.FFN_STAGES)]),
+                                       float(pst_mean[len(moesq.FFN_STAGES) + 3])),
             "roofline": {"bound": "mfma", "kernel": "k_gemm_prefill<gate_up>",
                          "achieved": round(ach, 2), "peak": F16_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(ach / F16_DENSE_PEAK_TFLOPS, 4), "traffic": None,

@@ -182,10 +182,12 @@ moesq_status moesq_route_topk(const void *logits, moesq_dtype dtype, int64_t T, 
 /* Profiling aid: with events (host array of n >= 5 hipEvent_t created by the caller) set, every later
  * moesq_moe_ffn call on this host thread records events[0] on its stream before its first kernel and
  * events[1..4] after the routing (permutation and gate/up input quantization), the gate/up GEMM (with
- * the fused SiLU*up and down-input quantization), the down GEMM and the top-k combine. With n >= 7,
- * events[5] and events[6] are recorded by the gate/up GEMM kernel's own dispatch, at its start and its
- * end (hipExtLaunchKernel), so they time that kernel alone, without launch gaps; on the one-launch path
- * events[1..4] all follow the single kernel and events[5..6] bracket it. NULL disables it.
+ * the fused SiLU*up and down-input quantization), the down GEMM and the top-k combine. With n >= 13,
+ * events[5 + 2i] and events[6 + 2i] are recorded by the kernels of stage i themselves (i = 0 routing,
+ * 1 gate/up GEMM, 2 down GEMM, 3 combine) through their own dispatch (hipExtLaunchKernel): the stage's
+ * first kernel records the start and its last kernel the end, so each pair times that stage's kernels
+ * without the launch gap before them. On the one-launch path events[1..4] all follow the single
+ * kernel, events[5..6] bracket it and events[7..12] are recorded right after it. NULL disables it.
  * The library keeps the pointer (thread-local) until it is reset; the caller keeps the array alive. */
 moesq_status moesq_set_stage_events(hipEvent_t *events /* host */, int32_t n);
 

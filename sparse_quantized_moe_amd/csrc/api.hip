@@ -11,10 +11,12 @@ thread_local std::string g_last_error;
 thread_local hipEvent_t* g_stage_events = nullptr;
 thread_local int g_stage_n = 0;
 
-// events[5], events[6] (when given) are recorded by the timed kernel itself, at its start and end
+// With 13 stage events, events[5 + 2 i] and events[6 + 2 i] are recorded by stage i's own kernels
+// (0 routing, 1 gate/up GEMM, 2 down GEMM, 3 combine), at the first one's start and the last one's end.
 struct TimedKernel {
-  explicit TimedKernel() {
-    if (g_stage_events && g_stage_n >= 7) moesq::kernel_events() = {g_stage_events[5], g_stage_events[6]};
+  explicit TimedKernel(int stage) {
+    if (g_stage_events && g_stage_n >= 13)
+      moesq::kernel_events() = {g_stage_events[5 + 2 * stage], g_stage_events[6 + 2 * stage]};
   }
   ~TimedKernel() { moesq::kernel_events() = {}; }
 };
@@ -272,18 +274,23 @@ moesq_status moesq_moe_ffn(const void* x, int64_t T, int32_t H, const int32_t* t
     stage_event(0, stream);
     hipError_t err;
     {
-      const TimedKernel timed;
+      const TimedKernel timed(0);
       err = moesq::launch_ffn_fused(f, stream);
     }
     for (int i = 1; i <= 4; ++i) stage_event(i, stream);
+    if (g_stage_events && g_stage_n >= 13)
+      for (int i = 7; i <= 12; ++i) stage_event(i, stream);   // the other stages: empty, after the kernel
     if (err != hipSuccess) return fail(MOESQ_ERR_HIP, "moe_ffn: fused launch: %s", hipGetErrorString(err));
     return check_launch(stream, (flags & MOESQ_FLAG_SYNC_CHECK) != 0);
   }
 
   // routing: permutation + gate/up input quantization (pair order)
   stage_event(0, stream);
-  moesq::launch_route(topk_ids, T, k, E, counts, offsets, tile_offsets, L.rows_per_mblock, sorted, inv, status,
-                      ws + L.route_scratch, static_cast<const uint16_t*>(x), H, a13_global, a13c, a13s, stream);
+  {
+    const TimedKernel timed(0);
+    moesq::launch_route(topk_ids, T, k, E, counts, offsets, tile_offsets, L.rows_per_mblock, sorted, inv, status,
+                        ws + L.route_scratch, static_cast<const uint16_t*>(x), H, a13_global, a13c, a13s, stream);
+  }
   stage_event(1, stream);
   // gate/up GEMM, row r reading activation row sorted[r]; fused silu * up and down-input quantization
   moesq::GemmParams g{};
@@ -291,7 +298,7 @@ moesq_status moesq_moe_ffn(const void* x, int64_t T, int32_t H, const int32_t* t
   g.a_rows = sorted; g.rows = P; g.w_packed = w13->packed; g.w_mask = w13->mask; g.w_scale = w13->scale; g.w_global = w13->global;
   g.E = E; g.N = w13->N; g.K = H; g.G = 2; g.layout = w13->layout; g.h_codes = a2c; g.h_scales = a2s; g.h_global = a2_global;
   {
-    const TimedKernel timed;
+    const TimedKernel timed(1);
     moesq::launch_grouped_gemm(g, moesq::kEpiGateUp, tactic, stream);
   }
   stage_event(2, stream);
@@ -299,9 +306,15 @@ moesq_status moesq_moe_ffn(const void* x, int64_t T, int32_t H, const int32_t* t
   d.a_codes = a2c; d.a_scales = a2s; d.a_global = a2_global; d.offsets = offsets; d.tile_offsets = tile_offsets;
   d.rows = P; d.w_packed = w2->packed; d.w_mask = w2->mask; d.w_scale = w2->scale; d.w_global = w2->global;
   d.E = E; d.N = H; d.K = I; d.G = 1; d.layout = w2->layout; d.out = drows; d.topk_weights = topk_weights; d.sorted = sorted;
-  moesq::launch_grouped_gemm(d, moesq::kEpiDown, tactic, stream);
+  {
+    const TimedKernel timed(2);
+    moesq::launch_grouped_gemm(d, moesq::kEpiDown, tactic, stream);
+  }
   stage_event(3, stream);
-  moesq::launch_combine(drows, inv, T, k, H, out, stream);
+  {
+    const TimedKernel timed(3);
+    moesq::launch_combine(drows, inv, T, k, H, out, stream);
+  }
   stage_event(4, stream);
   return check_launch(stream, (flags & MOESQ_FLAG_SYNC_CHECK) != 0);
 }

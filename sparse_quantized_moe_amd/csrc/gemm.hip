@@ -764,9 +764,9 @@ void launch_combine(const float* D, const int* inv, int64_t T, int k, int H, flo
   const int64_t n = T * (H >> 2);
   if (!n) return;
   const unsigned grid = (unsigned)((n + 255) / 256);
-  if (k <= 8) k_combine<8><<<grid, 256, 0, stream>>>(D, inv, T, k, H, out);
-  else if (k <= 16) k_combine<16><<<grid, 256, 0, stream>>>(D, inv, T, k, H, out);
-  else k_combine<32><<<grid, 256, 0, stream>>>(D, inv, T, k, H, out);
+  if (k <= 8) launch_kernel(k_combine<8>, dim3(grid), dim3(256), 0, stream, D, inv, T, k, H, out);
+  else if (k <= 16) launch_kernel(k_combine<16>, dim3(grid), dim3(256), 0, stream, D, inv, T, k, H, out);
+  else launch_kernel(k_combine<32>, dim3(grid), dim3(256), 0, stream, D, inv, T, k, H, out);
 }
 
 }  // namespace moesq

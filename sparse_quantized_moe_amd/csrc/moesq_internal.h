@@ -118,8 +118,10 @@ int64_t launch_probe_smfmac(int blocks, int iters, float* sink, hipStream_t stre
 // out[t][:] = sum_j D[inv[t*k + j]][:] (rows with inv < 0 skipped), in j order.
 void launch_combine(const float* D, const int* inv, int64_t T, int k, int H, float* out, hipStream_t stream);
 
-// Optional start/stop events that the next GEMM or one-launch FFN kernel records itself, at its own
-// start and end (hipExtLaunchKernelGGL), for timing that kernel alone; null: plain launches.
+// Optional start/stop events that the kernels of one FFN stage record themselves through their own
+// dispatch (hipExtLaunchKernelGGL): the stage's first kernel records the start, every kernel the end
+// (the last one's stands), so the pair times the stage's kernels without the launch gap before them.
+// Both null: plain launches.
 struct KernelEvents {
   hipEvent_t start = nullptr, stop = nullptr;
 };
@@ -127,11 +129,13 @@ KernelEvents& kernel_events();   // this host thread's
 
 template <typename F, typename... Args>
 inline void launch_kernel(F kernel, dim3 grid, dim3 block, size_t lds, hipStream_t stream, Args... args) {
-  const KernelEvents ev = kernel_events();
-  if (ev.start)
+  KernelEvents& ev = kernel_events();
+  if (ev.start || ev.stop) {
     hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, stream, ev.start, ev.stop, 0u, args...);
-  else
+    ev.start = nullptr;
+  } else {
     kernel<<<grid, block, lds, stream>>>(args...);
+  }
 }
 
 }  // namespace moesq

@@ -384,13 +384,13 @@ void launch_route(const int* ids, int64_t T, int k, int E, int* counts, int* off
     a.x = x; a.H = H; a.a_global = a_global; a.codes = codes; a.scales = scales;
   }
   const dim3 grid((unsigned)(a.ntiles + a.qblocks));
-  if (k <= 8) k_route<8><<<grid, kRouteThreads, route_lds_bytes(E), stream>>>(a);
-  else if (k <= 16) k_route<16><<<grid, kRouteThreads, route_lds_bytes(E), stream>>>(a);
-  else k_route<32><<<grid, kRouteThreads, route_lds_bytes(E), stream>>>(a);
+  if (k <= 8) launch_kernel(k_route<8>, grid, dim3(kRouteThreads), route_lds_bytes(E), stream, a);
+  else if (k <= 16) launch_kernel(k_route<16>, grid, dim3(kRouteThreads), route_lds_bytes(E), stream, a);
+  else launch_kernel(k_route<32>, grid, dim3(kRouteThreads), route_lds_bytes(E), stream, a);
   if (a.ntiles > 1) {
-    k_route_scan<<<1, kRouteThreads, (size_t)2 * E * 4, stream>>>(a);
+    launch_kernel(k_route_scan, dim3(1), dim3(kRouteThreads), (size_t)2 * E * 4, stream, a);
     const int64_t P = T * k;
-    k_route_scatter<<<(unsigned)((P + 255) / 256), 256, 0, stream>>>(a);
+    launch_kernel(k_route_scatter, dim3((unsigned)((P + 255) / 256)), dim3(256), 0, stream, a);
   }
 }
 
