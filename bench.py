@@ -255,6 +255,45 @@ def fold_figures(moesq, torch, ev, reps=20):
     return res
 
 
+def other_workloads(moesq, torch, ev, seed, dev, names=("e512_decode", "e512_prefill", "kimi_k2_prefill")):
+    """The other layer shapes, each timed on its own batch like the headline ones (no weight-copy
+    rotation: their touched weights are far larger than the 256 MB last-level cache): decode rows give
+    the weight-stream GB/s on the stored bytes of the touched experts, prefill rows the effective dense
+    TFLOP/s; both with each stage's kernel time."""
+    import synth
+    res = {}
+    for name in names:
+        wl = synth.WORKLOADS[name]
+        w13, w2, dense = build_layer(wl, seed, dev)
+        x, ids, wts, g13, g2 = batch(wl, seed, dev, dense)
+        ws = torch.empty(moesq.lib().moesq_moe_ffn_workspace_size(wl.T, wl.H, wl.I, wl.k, wl.E, 0),
+                         dtype=torch.uint8, device=dev)
+        out = torch.empty((wl.T, wl.H), dtype=torch.float32, device=dev)
+        decode = wl.T * wl.k <= 48 * wl.E
+        steps = 20 if decode else 5
+        a = (moesq, torch, ev, x, torch.from_numpy(ids).to(dev), torch.from_numpy(wts).to(dev), [(w13, w2)],
+             torch.from_numpy(g13).to(dev), torch.from_numpy(g2).to(dev), out, ws, 2, steps)
+        wall, _, _ = run_steps(*a)
+        _, st, _ = run_steps(*a, staged=True)
+        t = wall / steps
+        ns = len(moesq.FFN_STAGES)
+        r = {"tokens": wl.T, "experts": wl.E, "top_k": wl.k, "hidden": wl.H, "moe_intermediate": wl.I,
+             "us_per_step": round(t * 1e6, 2),
+             "kernel_us": {n: round(float(v) * 1e3, 2) for n, v in zip(moesq.FFN_STAGES, st.mean(axis=0)[ns:])}}
+        if decode:
+            n, wb = touched_bytes(ids, wl.E, wl.H, wl.I)
+            r.update({"metric": "weight-stream GB/s", "value": round(wb / t / 1e9, 2), "experts_touched": n,
+                      "stored_bytes_streamed": wb})
+        else:
+            P = int((ids >= 0).sum())
+            r.update({"metric": "effective dense TFLOP/s", "value": round(6.0 * P * wl.H * wl.I / t / 1e12, 2)})
+        log(f"{name}: {r['value']} {r['metric']}, {r['us_per_step']} us/step")
+        res[name] = r
+        del w13, w2, ws, out, x
+        torch.cuda.empty_cache()
+    return res
+
+
 def side_passes(wl, P, route_ms, combine_ms):
     """The two HBM-bound passes around the GEMMs, from their kernels' own start/end events: routing
     (router ids in; x in, bf16; activation codes and scales out; sorted and inv out) and the top-k
@@ -315,6 +354,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the 512-expert and 384-expert layers (timed after the headline ones)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run 3 plain device copies of MIB MiB (a known-size kernel for scaling HBM "
                          "byte counters under rocprofv3 --pmc)")
@@ -472,6 +513,11 @@ def main():
                          "measured_peak": peaks["smfmac_f16_kept_TFLOPs"],
                          "frac_of_measured": round(ach / peaks["smfmac_f16_kept_TFLOPs"], 4)},
         }
+
+    if not args.no_other_workloads:
+        del layers, w13, w2
+        torch.cuda.empty_cache()
+        result["other_workloads"] = other_workloads(moesq, torch, ev, args.seed, dev)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.seed, x, ids, wts, g13, g2, dense_expert, args.cpu_tokens)

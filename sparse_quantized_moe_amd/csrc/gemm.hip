@@ -672,6 +672,13 @@ static void set_lds_attr(Kern* k, size_t lds) {
 // several n-blocks and to hide each epilogue under the next n-block's loads
 constexpr int kNloopBlocks = 3;
 
+template <int EPI, int LAYOUT, int RT, int DEPTH>
+static void launch_nloop(const GemmParams& p, dim3 grid, int nblocks, hipStream_t stream) {
+  const size_t lds = DecGeom<DEPTH>::lds;
+  set_lds_attr(&k_gemm_decode_nloop<EPI, LAYOUT, RT, DEPTH>, lds);
+  launch_kernel(k_gemm_decode_nloop<EPI, LAYOUT, RT, DEPTH>, grid, dim3(kGemmThreads), lds, stream, p, nblocks);
+}
+
 template <int EPI, int LAYOUT>
 static void launch_decode(const GemmParams& p, hipStream_t stream) {
   // gate/up waves own 4 row-tiles (32 columns for the fused quantization); other linears stream
@@ -691,13 +698,15 @@ static void launch_decode(const GemmParams& p, hipStream_t stream) {
   }
   const int nblocks = EPI == kEpiGateUp ? ((p.N >> 1) + 127) / 128 : (p.N + 64 * RT - 1) / (64 * RT);
   if constexpr (EPI != kEpiGateUp) {
-    if (p.K == DEPTH * 256) {
-      const size_t lds = DecGeom<DEPTH>::lds;
-      set_lds_attr(&k_gemm_decode_nloop<EPI, LAYOUT, RT, DEPTH>, lds);
-      const int ny = (nblocks + kNloopBlocks - 1) / kNloopBlocks;
-      launch_kernel(k_gemm_decode_nloop<EPI, LAYOUT, RT, DEPTH>, dim3((unsigned)p.E, (unsigned)ny), dim3(kGemmThreads), lds,
-                    stream, p, nblocks);
-      return;
+    // K up to 1024: the whole K staged once and the ring holding one n-block's K (K / 256 slots)
+    const int ny = (nblocks + kNloopBlocks - 1) / kNloopBlocks;
+    const dim3 grid((unsigned)p.E, (unsigned)ny);
+    switch (p.K) {
+      case 256: launch_nloop<EPI, LAYOUT, RT, 1>(p, grid, nblocks, stream); return;
+      case 512: launch_nloop<EPI, LAYOUT, RT, 2>(p, grid, nblocks, stream); return;
+      case 768: launch_nloop<EPI, LAYOUT, RT, 3>(p, grid, nblocks, stream); return;
+      case 1024: launch_nloop<EPI, LAYOUT, RT, 4>(p, grid, nblocks, stream); return;
+      default: break;
     }
   }
   const size_t lds = DecGeom<DEPTH>::lds;
