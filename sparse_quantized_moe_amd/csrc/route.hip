@@ -146,13 +146,15 @@ __device__ void route_tile(const RouteArgs& a, int tile, uint8_t* smem) {
   if (tid == 0) { s_bad = 0; s_dup = 0; }
   __syncthreads();
   if (valid) {
+    // a token naming an expert twice is found by comparing its ids (the mask bits only say "some")
     int bad = 0, dup = 0;
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
       const int e = ids[j];
       if (e < 0 || e >= E) { bad += e != -1; continue; }
-      const unsigned long long old = atomicOr(&wmask[wv * E + e], bit);
-      dup |= (old & bit) != 0ull;
+      atomicOr(&wmask[wv * E + e], bit);
+#pragma unroll
+      for (int i = 0; i < j; ++i) dup |= ids[i] == e;
     }
     if (bad) atomicAdd(&s_bad, bad);
     if (dup) s_dup = 1;
@@ -219,19 +221,38 @@ __device__ void route_tile(const RouteArgs& a, int tile, uint8_t* smem) {
   // else straight to memory
   const int64_t P = a.T * k;
   const bool staged = P <= kRouteStagePairs;
-  int* dst_sorted = staged ? s_sorted : a.sorted;
-  int* dst_inv = staged ? s_inv : a.inv;
   if (valid) {
+    // every rank first (reads only), then the writes; the two destinations are written by separate
+    // code so that each store has a known address space (LDS or global, not flat)
+    int rr[KMAX];
+    if (serial) {
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      if (j >= k) continue;
-      const int64_t p = t * k + j;
-      const int e = ids[j];
-      if (e < 0 || e >= E) { dst_inv[p] = -1; continue; }
-      const int r = cnt[e] + rank_of(p, e);
-      dst_sorted[r] = (int)p;
-      dst_inv[p] = r;
+      for (int j = 0; j < KMAX; ++j) {
+        const int e = ids[j];
+        rr[j] = (j < k && e >= 0 && e < E) ? cnt[e] + a.inv[t * k + j] : -1;
+      }
+    } else {   // LDS only: no wait on the global stores above
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        const int e = ids[j];
+        rr[j] = (j < k && e >= 0 && e < E)
+                    ? cnt[e] + wbase[wv * E + e] + (int)__builtin_popcountll(wmask[wv * E + e] & below)
+                    : -1;
+      }
     }
+    auto scatter = [&](int* dst_sorted, int* dst_inv) {
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        if (j >= k) continue;
+        const int64_t p = t * k + j;
+        dst_inv[p] = rr[j];
+        if (rr[j] >= 0) dst_sorted[rr[j]] = (int)p;
+      }
+    };
+    if (staged)
+      scatter(s_sorted, s_inv);
+    else
+      scatter(a.sorted, a.inv);
   }
   if (staged) {
     __syncthreads();
