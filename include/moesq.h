@@ -7,9 +7,9 @@
  * with MOESQ_FLAG_SYNC_CHECK). The library never allocates or frees device memory in these calls and
  * keeps no pointer after return; the caller owns every buffer, including workspaces, and keeps it
  * alive until the stream work is done. No C++ exception crosses this boundary. The calls keep no
- * global mutable state apart from a one-time kernel attribute set-up and two thread-local values
- * (the text of moesq_last_error() and the profiling events of moesq_set_stage_events()), so they
- * are reentrant.
+ * global mutable state apart from a one-time kernel attribute set-up and thread-local values (the
+ * text of moesq_last_error(), the profiling events of moesq_set_stage_events(), and inside a
+ * moesq_moe_ffn call the events its kernels record), so they are reentrant.
  *
  * Errors: a synchronous argument check returns a negative moesq_status and enqueues nothing; a launch
  * failure returns MOESQ_ERR_HIP with the HIP error text in moesq_last_error().
@@ -102,8 +102,9 @@ moesq_status moesq_quantize_act(const void *x, moesq_dtype x_dtype, int64_t rows
                                 const int32_t *expert_offsets, int32_t E, const float *global,
                                 uint8_t *codes, uint8_t *scales, hipStream_t stream);
 
-/* Stable grouping of the router's (token, slot) pairs p = t*k + j by expert id (the grouped GEMM runs
- * one GEMM per expert over its rows).
+/* Stable grouping of the router's (token, slot) pairs p = t*k + j by expert id (model card
+ * "Qwen3.5-397B-A17B-P48NVFP4-MoESQ": each token is routed to its top-k experts and the expert kernel
+ * is a grouped GEMM, one GEMM per expert over the rows routed to it).
  *   topk_ids [T][k] int32 in [0, E), or -1 to drop the pair (ids outside [-1, E) are also dropped and
  *            counted in *status).
  *   counts [E], offsets [E+1] (exclusive prefix of counts), sorted [T*k] (the offsets[E] live pair ids
@@ -128,7 +129,9 @@ moesq_status moesq_grouped_gemm(const uint8_t *a_codes, const uint8_t *a_scales,
                                 const int32_t *expert_offsets, int64_t rows, const moesq_weights *w,
                                 float *out, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* MoE FFN of T tokens through the routed experts (the W4A4 paired-4:8 expert path):
+/* MoE FFN of T tokens through the routed experts (model cards "Qwen3.5-397B-A17B-P48NVFP4-MoESQ" and
+ * "Qwen3-30B-A3B-P48NVFP4-MoESQ", "Compression details": gate_proj, up_proj and down_proj of every
+ * routed expert in W4A4 NVFP4 with paired-4:8 weights, activations quantized per expert linear):
  *   for each pair (t, j) with e = topk_ids[t][j] >= 0:
  *     a13 = NVFP4(x[t], a13_global[e]);  [gate | up] = a13 @ W13_e^T;  h = silu(gate) * up
  *     a2  = NVFP4(h, a2_global[e]);      y = a2 @ W2_e^T

@@ -9,14 +9,18 @@ What it states, each function citing the passage it follows:
 * ``nvfp4``      E2M1 / E4M3FN codecs and the per-32 NVFP4 quantizer (model cards, "Compression details").
 * ``pairbitmask`` the pair-bitmask storage codec (model cards, "Sparse storage layout").
 * ``compress``   synthetic weight compression: paired-4:8 magnitude prune, NVFP4, pack.
-* ``moe``        the token->expert permutation, the grouped GEMM and the MoE FFN with top-k combine.
+* ``moe``        the router (softmax top-k), the token->expert permutation, the grouped GEMM, the
+                 load-time gate/up global fold and the MoE FFN with top-k combine.
 
 Every value is computed in float64 from exact inputs; see each docstring for why that reaches the exact
 decision where an integer (a code or a scale byte) is decided by a real-valued comparison.
 
-Parity status: the codecs, the quantizer, the codec of the storage format, the prune, the permutation
-and the grouped GEMM are pinned by tests against textbook tables, a library cast, exact-rational brute
-force, hand-derived fixtures and the pages' storage figures. The end-to-end FFN is a composition of
-pinned stages plus libm ``exp`` and is otherwise pinned only by metamorphic relations.
+Parity status: the codecs, the quantizer, the codec of the storage format, the prune, the permutation,
+the grouped GEMM, the router and the gate/up fold are pinned by tests against textbook tables, a
+library cast, exact-rational brute force, rank counts, closed forms, hand-derived fixtures and the
+pages' storage figures. ``moe.moe_ffn``: parity unpinned as a whole -- it is a composition of the
+pinned stages plus libm ``exp``, and beyond that only metamorphic relations hold it (top-1 equals the
+single-expert FFN, token shuffles permute the rows, top-k is the weighted sum of top-1 runs); the
+pages print no worked FFN example.
 """
 from . import nvfp4, pairbitmask, compress, moe  # noqa: F401

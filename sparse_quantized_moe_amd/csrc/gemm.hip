@@ -227,9 +227,9 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(3)
     GemmParams p, int nblocks) {
   constexpr int TG = kDecTG, BMT = kDecBMT;
   using Geo = DecGeom<DEPTH>;
-  constexpr int RS = Geo::RS, KC = Geo::KC, IPT = Geo::IPT;
+  constexpr int RS = Geo::RS, IPT = Geo::IPT;
   extern __shared__ __align__(16) uint8_t smem[];
-  const int K = p.K;                                              // == KC
+  const int K = p.K;                                              // == Geo::KC
   uint8_t* sB = smem;                                             // [BMT][RS] f16
   uint16_t* lut_idx = reinterpret_cast<uint16_t*>(smem + BMT * RS);   // [256]
   __shared__ int s_arow[BMT];
