@@ -668,9 +668,11 @@ static void set_lds_attr(Kern* k, size_t lds) {
   }
 }
 
-// n-blocks per workgroup of the one-chunk decode kernel: enough to stage the activations once for
-// several n-blocks and to hide each epilogue under the next n-block's loads
-constexpr int kNloopBlocks = 3;
+// Workgroups per expert of the one-chunk decode kernel, and the fewest n-blocks one covers: enough
+// n-blocks per workgroup to stage the activations once for several of them and to hide each epilogue
+// under the next n-block's loads (measured best: 4 workgroups per expert at 16 and at 32 n-blocks).
+constexpr int kNloopGroups = 4;
+constexpr int kNloopMinBlocks = 4;
 
 template <int EPI, int LAYOUT, int RT, int DEPTH>
 static void launch_nloop(const GemmParams& p, dim3 grid, int nblocks, hipStream_t stream) {
@@ -699,7 +701,9 @@ static void launch_decode(const GemmParams& p, hipStream_t stream) {
   const int nblocks = EPI == kEpiGateUp ? ((p.N >> 1) + 127) / 128 : (p.N + 64 * RT - 1) / (64 * RT);
   if constexpr (EPI != kEpiGateUp) {
     // K up to 1024: the whole K staged once and the ring holding one n-block's K (K / 256 slots)
-    const int ny = (nblocks + kNloopBlocks - 1) / kNloopBlocks;
+    int per = (nblocks + kNloopGroups - 1) / kNloopGroups;
+    per = per < kNloopMinBlocks ? kNloopMinBlocks : per;
+    const int ny = (nblocks + per - 1) / per;
     const dim3 grid((unsigned)p.E, (unsigned)ny);
     switch (p.K) {
       case 256: launch_nloop<EPI, LAYOUT, RT, 1>(p, grid, nblocks, stream); return;
