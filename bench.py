@@ -351,7 +351,9 @@ def main():
     ap.add_argument("--workload", default="qwen3_30b_decode")
     ap.add_argument("--prefill-workload", default="qwen3_30b_prefill", help="'' to skip the prefill figure")
     ap.add_argument("--copies", type=int, default=4, help="weight copies rotated at decode (cache-cold stream)")
-    ap.add_argument("--cpu-tokens", type=int, default=8)
+    ap.add_argument("--cpu-tokens", type=int, default=64,
+                    help="tokens of the decode batch the oracle baseline runs on (about 6-7 s of CPU work: nearly "
+                         "every expert is touched, and the per-expert dequantization dominates)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-other-workloads", action="store_true",
