@@ -443,6 +443,44 @@ def test_moe_ffn_fused_matches_separate_launches(case):
     assert int(it_f["status"][0]) == int(((ids < -1) | (ids >= E)).sum())
 
 
+@pytest.mark.parametrize("flags", [0, moesq.FLAG_FUSED])
+def test_stage_events_time_the_kernels(flags):
+    """moesq_set_stage_events with 13 events: the five stage events bracket the stages and every
+    stage's kernels record their own start/end pair (hipExtLaunchKernel); each kernel pair lies
+    inside its stage interval, and the outputs are those of a call without events."""
+    import bench
+    E, H, I, T, k = 8, 512, 256, 64, 4
+    w13, w2, dense_expert = _layer(41, E, H, I)
+    x = synth.activations(42, T, H, device=DEV)
+    ids, wts = synth.routing(43, T, E, k)
+    g13, g2 = _globals(x, ids, E, dense_expert)
+    args = (x, torch.from_numpy(ids).to(DEV), torch.from_numpy(wts).to(DEV), w13, w2,
+            torch.from_numpy(g13).to(DEV), torch.from_numpy(g2).to(DEV))
+    ref = moesq.moe_ffn(*args, flags=flags).cpu()
+    ev = bench.HipEvents()
+    evs = ev.create(13)
+    try:
+        moesq.set_stage_events(evs)
+        out = moesq.moe_ffn(*args, flags=flags)
+        moesq.set_stage_events(None)
+        torch.cuda.synchronize()
+        stage = [ev.elapsed_ms(evs[j], evs[j + 1]) for j in range(4)]
+        kern = [ev.elapsed_ms(evs[5 + 2 * j], evs[6 + 2 * j]) for j in range(4)]
+        fused = moesq.ffn_layout(T, H, I, k, E, flags)["fused"] == 1
+        if fused:
+            # one kernel: its pair lies inside the whole call; the other pairs are back-to-back event
+            # records after it, as short as the (empty) stage intervals that follow the kernel
+            assert 0.0 < kern[0] <= sum(stage) + 1e-3, (stage, kern)
+            assert all(t <= max(stage[1:]) + 1e-3 for t in kern[1:]), (stage, kern)
+        else:
+            for s_ms, k_ms in zip(stage, kern):
+                assert 0.0 < k_ms <= s_ms + 1e-3, (stage, kern)
+        assert torch.equal(out.cpu(), ref)
+    finally:
+        moesq.set_stage_events(None)
+        ev.destroy(evs)
+
+
 def test_probe_smfmac_counts_and_writes():
     """The MFMA throughput probe issues blocks x 4 waves x iters x 32 instructions and writes its sink."""
     sink = torch.full((4 * 256,), float("nan"), dtype=torch.float32, device=DEV)
