@@ -540,8 +540,14 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_prefill(GemmParams p) {
   if (tid < BMT) {
     const int r = row0 + m0 + tid;
     s_arow[tid] = tid < mrows ? (p.a_rows ? p.a_rows[r] : r) : 0;
-    if (EPI == kEpiDown) s_rw[tid] = tid < mrows ? row_weight(p, r) : 0.0f;
   }
+  // down: the rows' router weights (topk_weights[sorted[r]], two dependent loads) are loaded under
+  // the K loop's first steps and staged in LDS for the epilogue only
+  int rw_pair = 0;
+  float rw = 0.0f;
+  const bool rw_live = EPI == kEpiDown && tid < mrows;
+  auto rw_first = [&]() { if (rw_live) rw_pair = p.sorted[row0 + m0 + tid]; };
+  auto rw_second = [&]() { if (rw_live) rw = p.topk_weights[rw_pair]; };
   const EpiScalars es = epi_scalars<EPI>(p, e);
 
   int wrow[4];
@@ -633,14 +639,24 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_prefill(GemmParams p) {
   for (; gs + 2 <= nsteps; gs += 2) {
     commit(ac);
     prefetch(gs + 1, ac);
+    if (gs == 0) rw_first();
     step(w0, gs + 2);
     commit(ac);
     prefetch(gs + 2, ac);
+    if (gs == 0) rw_second();
     step(w1, gs + 3);
   }
   if (gs < nsteps) {                               // odd step count: the last step
     commit(ac);
+    if (gs == 0) {                                 // a single step: the router weights now
+      rw_first();
+      rw_second();
+    }
     step(w0, -1);
+  }
+  if constexpr (EPI == kEpiDown) {
+    if (tid < BMT) s_rw[tid] = rw;                 // rows past the m-block: 0
+    __syncthreads();
   }
   if (!active) return;
   gemm_epilogue<EPI, TG>(p, es, acc, row0, m0, mrows, nb, wv, wrow, s_rw, lane);
