@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define MOESQ_ABI_VERSION 4
+#define MOESQ_ABI_VERSION 5
 /* quantization_config marker "paired48_sparse": {"layout": "pair-bitmask", "version": 1} */
 #define MOESQ_PAIR_BITMASK_VERSION 1
 
@@ -63,9 +63,11 @@ typedef enum { MOESQ_BF16 = 0, MOESQ_F32 = 1 } moesq_dtype;
  *   `packed` points to E * (N/16) * (K/256) records of 1408 bytes, ordered [expert][16-row tile]
  *   [256-K step]. Record lane l (row l % 16 of the tile, 64-K quarter q = l / 16 of the step) holds
  *   at 16*l the 16 kept bytes of its 64 K (every 4 bytes = two chunks (b0 b1)(b0' b1') rewritten as
- *   (lo b0 | lo b1 << 4, hi b0 | hi b1 << 4, lo b0' | lo b1' << 4, hi b0' | hi b1' << 4)), at
- *   1024 + 4*l its 4 mask bytes and at 1280 + 2*l its 2 scale bytes. mask and scale are unused (NULL).
- *   Requires K % 256 == 0 and N % 16 == 0; moesq_prepare_weights / moesq_unprepare_weights convert. */
+ *   (lo b0 | lo b1 << 4, lo b0' | lo b1' << 4, hi b0 | hi b1 << 4, hi b0' | hi b1' << 4)), at
+ *   1024 + 4*l its 4 mask bytes with each nibble replaced by the position code i0 | i1 << 2 of its
+ *   two set bits i0 < i1, and at 1280 + 2*l its 2 scale bytes. mask and scale are unused (NULL).
+ *   Requires K % 256 == 0 and N % 16 == 0; moesq_prepare_weights / moesq_unprepare_weights convert
+ *   (exactly for masks whose nibbles have two bits set, as the format requires). */
 #define MOESQ_LAYOUT_PAIR_BITMASK 0
 #define MOESQ_LAYOUT_TILED 1
 

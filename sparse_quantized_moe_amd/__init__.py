@@ -26,7 +26,7 @@ __all__ = [
 _PKG = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_PKG, "libmoesq.so")
 #: The C ABI version (MOESQ_ABI_VERSION in include/moesq.h) these bindings are declared for.
-ABI_VERSION = 4
+ABI_VERSION = 5
 FLAG_SYNC_CHECK = 1
 FLAG_UNFUSED = 2      # moe_ffn: separate launches even where the one-launch decode path applies
 FLAG_FUSED = 4        # moe_ffn: the one-launch decode path wherever it applies

@@ -71,7 +71,7 @@ struct FusedArgs {
 };
 
 __host__ __device__ constexpr size_t fused_lds_bytes(int H, int I, int P) {
-  return (size_t)kFzBMT * (2 * (H > I ? H : I) + 16) + 512 + (size_t)P * 4;
+  return (size_t)kFzBMT * (2 * (H > I ? H : I) + 16) + (size_t)P * 4;
 }
 
 // Workgroup barrier that orders LDS only: a wave with global loads in flight does not wait for them
@@ -176,12 +176,12 @@ __device__ __forceinline__ void fz_stage(__amdgpu_buffer_rsrc_t c_rsrc, __amdgpu
       const int i = i0 + tid + j * NT;
       const int n = i % kFzBMT, q = i / kFzBMT;
       if (n < ntiles * 16 && q < G) {
-        const f16 svh = e4m3_to_f16(sv[j]);
-        const f16x2 s2 = f16x2{svh, svh};
-        const uint32_t wv4[4] = {cv[j].x, cv[j].y, cv[j].z, cv[j].w};
+        const f16x2 s2 = scale_bcast_f16(sv[j]);
+        u32x4 u4[4];
+        act_group_kprime(cv[j], s2, u4);
 #pragma unroll
         for (int h = 0; h < 4; ++h)
-          *reinterpret_cast<u32x4*>(sB + n * RS + (4 * q + h) * 16) = act_chunk_kprime(wv4[h], s2);
+          *reinterpret_cast<u32x4*>(sB + n * RS + (4 * q + h) * 16) = u4[h];
       }
     }
   }
@@ -190,7 +190,7 @@ __device__ __forceinline__ void fz_stage(__amdgpu_buffer_rsrc_t c_rsrc, __amdgpu
 // The MFMAs of one 256-K super-step `gs` of weight fragment w against the staged rows; once the last
 // word of w is decoded, w is reloaded through `reload` (a callable taking the fragment).
 template <int RT, class Reload>
-__device__ __forceinline__ void fz_step(const uint8_t* sB, int RS, int gs, int ntiles, const uint16_t* lut,
+__device__ __forceinline__ void fz_step(const uint8_t* sB, int RS, int gs, int ntiles,
                                         WeightFrag<RT>& w, f32x4 (&acc)[RT][kFzTG], Reload reload) {
   const int lane = threadIdx.x & 63, nrow = lane & 15, qb = lane >> 4;
 #pragma unroll
@@ -202,7 +202,7 @@ __device__ __forceinline__ void fz_step(const uint8_t* sB, int RS, int gs, int n
       const f16x2 sp = scale_pair_f16(w.sc[rt]);
       const f16x2 s2 = (t < 2) ? __builtin_shufflevector(sp, sp, 0, 0) : __builtin_shufflevector(sp, sp, 1, 1);
       A[rt] = weight_operand_tiled(frag_word(w.pk[rt], t), s2);
-      idx[rt] = lut[(w.mk[rt] >> (8 * t)) & 255u];
+      idx[rt] = smfmac_index_of_codes(w.mk[rt], t);
     }
     if (t == 3) {
       slot_decoded<RT>(A, idx);
@@ -238,8 +238,7 @@ __global__ __launch_bounds__(kFzThreads) __attribute__((amdgpu_waves_per_eu(3)))
   const int P = a.T * k;
   const int RSmax = 2 * (H > I ? H : I) + 16;
   uint8_t* sB = smem;                                                    // [kFzBMT][RSmax] staging
-  uint16_t* lut = reinterpret_cast<uint16_t*>(smem + kFzBMT * RSmax);    // [256]
-  int* s_rows = reinterpret_cast<int*>(lut + 256);                       // [P]: pairs of expert e, in order
+  int* s_rows = reinterpret_cast<int*>(smem + kFzBMT * RSmax);           // [P]: pairs of expert e, in order
   __shared__ int s_wcnt[kFzWaves];
   __shared__ int s_sum[3];                                               // matches, smaller ids, dropped ids
   __shared__ float s_rw[kFzBMT];
@@ -298,7 +297,6 @@ __global__ __launch_bounds__(kFzThreads) __attribute__((amdgpu_waves_per_eu(3)))
   }
 
   // ---- routing phase
-  if (tid < 256) lut[tid] = (uint16_t)smfmac_index_of_mask_byte((uint32_t)tid);
   float* s_g = reinterpret_cast<float*>(sB);                             // staging area, free until then
   for (int i = tid; i < E; i += kFzThreads) s_g[i] = i == tid ? gval : a.a13_global[i];
   if (tid < 3) s_sum[tid] = 0;
@@ -420,11 +418,11 @@ __global__ __launch_bounds__(kFzThreads) __attribute__((amdgpu_waves_per_eu(3)))
 #pragma unroll
         for (int d = 0; d < 2; ++d) {
           const int rl = gs + 2 + d;
-          fz_step<4>(sB, RS, gs + d, ntiles, lut, wg[d], acc,
+          fz_step<4>(sB, RS, gs + d, ntiles, wg[d], acc,
                      [&](WeightFrag<4>& w) { wpg.load(rl, w, active_g && rl < nsg); });
         }
       }
-      if (gs < nsg) fz_step<4>(sB, RS, gs, ntiles, lut, wg[0], acc, [&](WeightFrag<4>&) {});
+      if (gs < nsg) fz_step<4>(sB, RS, gs, ntiles, wg[0], acc, [&](WeightFrag<4>&) {});
       if (active_g)
         gemm_epilogue<kEpiGateUp, kFzTG, 4, kCpolDevice>(gp, es, acc, row0, m0, mrows, 0, gw, wrow_g, s_rw, lane);
     }
@@ -514,7 +512,7 @@ __global__ __launch_bounds__(kFzThreads) __attribute__((amdgpu_waves_per_eu(3)))
           const int rec = r0 + d;
           if (rec < nrec) {
             const int rl = rec + kFzDownDepth;
-            fz_step<kFzDownRT>(sB, RSd, rec % nsd, ntiles, lut, wd[d], acc,
+            fz_step<kFzDownRT>(sB, RSd, rec % nsd, ntiles, wd[d], acc,
                                [&](WeightFrag<kFzDownRT>& w) { load_rec(rl, w); });
             if (rec % nsd == nsd - 1) {
               int wrow[2];

@@ -8,7 +8,8 @@
 // stored as 16 x 32 kept values + a 2-bit position per kept value); the activations are the dense
 // operand B (64 K x 16 tokens). In the K' order of moesq_device.h every 4-group holds exactly 2
 // kept values, so the kept bytes of the pair-bitmask storage ARE the compressed operand (low nibbles
-// for the even group, high nibbles for the odd group) and the mask nibble gives both groups' index.
+// for the even groups, high nibbles for the odd groups) and a chunk's mask nibble gives the index of
+// both its groups (tiled weights carry that index code in place of the nibble).
 // Dequantization is exact: e2m1 * e4m3 has <= 6 significant bits, so it is exact in f16, products
 // of two such values are exact in fp32 and accumulation is in fp32. Global scales are applied in the
 // fp32 epilogue.
@@ -88,7 +89,7 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(3)
   const int M = p.offsets[e + 1] - row0;
   if (M <= 0) return;
   const EpiScalars es = epi_scalars<EPI>(p, e);
-  lut_idx[tid] = (uint16_t)smfmac_index_of_mask_byte((uint32_t)tid);
+  if (LAYOUT == 0) lut_idx[tid] = (uint16_t)smfmac_index_of_mask_byte((uint32_t)tid);
 
   int wrow[RT];
   const bool active = wave_rows<EPI, RT>(p.N, nb, wv, wrow);
@@ -138,12 +139,12 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(3)
       if (sn < ntiles * 16) {
 #pragma unroll
         for (int j = 0; j < IPT; ++j) {
-          const f16 sv = e4m3_to_f16(ac.s[j]);
-          const f16x2 s2 = f16x2{sv, sv};
-          const uint32_t wv4[4] = {ac.v[j].x, ac.v[j].y, ac.v[j].z, ac.v[j].w};
+          const f16x2 s2 = scale_bcast_f16(ac.s[j]);
+          u32x4 u4[4];
+          act_group_kprime(ac.v[j], s2, u4);
 #pragma unroll
-          for (int h = 0; h < 4; ++h)                               // 8-K chunk 4 (sq0 + j) + h
-            *reinterpret_cast<u32x4*>(sB + sn * RS + (4 * (sq0 + j) + h) * 16) = act_chunk_kprime(wv4[h], s2);
+          for (int h = 0; h < 4; ++h)                               // LDS unit 4 (sq0 + j) + h
+            *reinterpret_cast<u32x4*>(sB + sn * RS + (4 * (sq0 + j) + h) * 16) = u4[h];
         }
       }
       __syncthreads();
@@ -165,7 +166,7 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(3)
           const f16x2 sp = scale_pair_f16(w.sc[rt]);
           const f16x2 s2 = (t < 2) ? __builtin_shufflevector(sp, sp, 0, 0) : __builtin_shufflevector(sp, sp, 1, 1);
           A[rt] = weight_operand_of<LAYOUT>(frag_word(w.pk[rt], t), s2);
-          idx[rt] = lut_idx[(w.mk[rt] >> (8 * t)) & 255u];
+          idx[rt] = sparse_index<LAYOUT>(w.mk[rt], t, lut_idx);
         }
         if (t == 3 && reload >= 0) {
           slot_decoded<RT>(A, idx);
@@ -243,7 +244,7 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(3)
   const int M = p.offsets[e + 1] - row0;
   if (M <= 0 || nb0 >= nb1) return;
   const EpiScalars es = epi_scalars<EPI>(p, e);
-  lut_idx[tid] = (uint16_t)smfmac_index_of_mask_byte((uint32_t)tid);
+  if (LAYOUT == 0) lut_idx[tid] = (uint16_t)smfmac_index_of_mask_byte((uint32_t)tid);
   const int nrow = lane & 15, qb = lane >> 4;
   const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(p.a_codes), (short)0, (int)(p.rows * (K >> 1)), kBufferRsrcWord3);
@@ -288,12 +289,12 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(3)
     if (sn < ntiles * 16) {
 #pragma unroll
       for (int j = 0; j < IPT; ++j) {
-        const f16 sv = e4m3_to_f16(ac.s[j]);
-        const f16x2 s2 = f16x2{sv, sv};
-        const uint32_t wv4[4] = {ac.v[j].x, ac.v[j].y, ac.v[j].z, ac.v[j].w};
+        const f16x2 s2 = scale_bcast_f16(ac.s[j]);
+        u32x4 u4[4];
+        act_group_kprime(ac.v[j], s2, u4);
 #pragma unroll
         for (int h = 0; h < 4; ++h)
-          *reinterpret_cast<u32x4*>(sB + sn * RS + (4 * (sq0 + j) + h) * 16) = act_chunk_kprime(wv4[h], s2);
+          *reinterpret_cast<u32x4*>(sB + sn * RS + (4 * (sq0 + j) + h) * 16) = u4[h];
       }
     }
     __syncthreads();
@@ -319,7 +320,7 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(3)
             const f16x2 sp = scale_pair_f16(w[d].sc[rt]);
             const f16x2 s2 = (t < 2) ? __builtin_shufflevector(sp, sp, 0, 0) : __builtin_shufflevector(sp, sp, 1, 1);
             A[rt] = weight_operand_of<LAYOUT>(frag_word(w[d].pk[rt], t), s2);
-            idx[rt] = lut_idx[(w[d].mk[rt] >> (8 * t)) & 255u];
+            idx[rt] = sparse_index<LAYOUT>(w[d].mk[rt], t, lut_idx);
           }
           if (t == 3) {                                             // the next n-block's step d
             slot_decoded<RT>(A, idx);
@@ -362,7 +363,7 @@ constexpr int kStreamThreads = kStreamWaves * 64;
 constexpr int kStreamMaxK = 2048;
 constexpr int kStreamItems = (kDecBMT * (kStreamMaxK / 32) + kStreamThreads - 1) / kStreamThreads;  // staging items per thread
 
-__host__ __device__ constexpr size_t stream_lds_bytes(int K) { return (size_t)kDecBMT * (K * 2 + 16) + 512; }
+__host__ __device__ constexpr size_t stream_lds_bytes(int K) { return (size_t)kDecBMT * (K * 2 + 16); }
 
 template <int EPI, int RT, int DEPTH>
 __global__ __launch_bounds__(kStreamThreads) __attribute__((amdgpu_waves_per_eu(3))) void k_gemm_decode_stream(GemmParams p) {
@@ -370,7 +371,6 @@ __global__ __launch_bounds__(kStreamThreads) __attribute__((amdgpu_waves_per_eu(
   extern __shared__ __align__(16) uint8_t smem[];
   const int K = p.K, RS = K * 2 + 16;
   uint8_t* sB = smem;                                                     // [BMT][RS] f16
-  uint16_t* lut_idx = reinterpret_cast<uint16_t*>(smem + BMT * RS);       // [256]
   __shared__ int s_arow[BMT];
   __shared__ float s_rw[BMT];
 
@@ -381,7 +381,6 @@ __global__ __launch_bounds__(kStreamThreads) __attribute__((amdgpu_waves_per_eu(
   const int M = p.offsets[e + 1] - row0;
   if (M <= 0) return;
   const EpiScalars es = epi_scalars<EPI>(p, e);
-  if (tid < 256) lut_idx[tid] = (uint16_t)smfmac_index_of_mask_byte((uint32_t)tid);
   int wrow[RT];
   const bool active = wave_rows<EPI, RT>(p.N, 0, gw, wrow);
   WeightPtrs<1, RT> wp;
@@ -429,12 +428,12 @@ __global__ __launch_bounds__(kStreamThreads) __attribute__((amdgpu_waves_per_eu(
         const int i = tid + j * kStreamThreads;
         const int n = i % BMT, q = i / BMT;
         if (n < ntiles * 16 && q < G) {
-          const f16 svh = e4m3_to_f16(sv[j]);
-          const f16x2 s2 = f16x2{svh, svh};
-          const uint32_t wv4[4] = {cv[j].x, cv[j].y, cv[j].z, cv[j].w};
+          const f16x2 s2 = scale_bcast_f16(sv[j]);
+          u32x4 u4[4];
+          act_group_kprime(cv[j], s2, u4);
 #pragma unroll
           for (int h = 0; h < 4; ++h)
-            *reinterpret_cast<u32x4*>(sB + n * RS + (4 * q + h) * 16) = act_chunk_kprime(wv4[h], s2);
+            *reinterpret_cast<u32x4*>(sB + n * RS + (4 * q + h) * 16) = u4[h];
         }
       }
     }
@@ -456,7 +455,7 @@ __global__ __launch_bounds__(kStreamThreads) __attribute__((amdgpu_waves_per_eu(
           const f16x2 sp = scale_pair_f16(w.sc[rt]);
           const f16x2 s2 = (t < 2) ? __builtin_shufflevector(sp, sp, 0, 0) : __builtin_shufflevector(sp, sp, 1, 1);
           A[rt] = weight_operand_tiled(frag_word(w.pk[rt], t), s2);
-          idx[rt] = lut_idx[(w.mk[rt] >> (8 * t)) & 255u];
+          idx[rt] = smfmac_index_of_codes(w.mk[rt], t);
         }
         if (t == 3 && reload >= 0) {
           slot_decoded<RT>(A, idx);
@@ -529,7 +528,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_prefill(GemmParams p) {
   const int w_item = (int)(blockIdx.x % kXcds) * per + xi;
   if (xi >= per || w_item >= items) return;
   const int mb = w_item / nblocks, nb = w_item - mb * nblocks;
-  lut[tid] = (uint16_t)smfmac_index_of_mask_byte((uint32_t)tid);
+  if (LAYOUT == 0) lut[tid] = (uint16_t)smfmac_index_of_mask_byte((uint32_t)tid);
   const int e = find_expert(p.tile_offsets, p.E, mb, &s_e);
   if (e < 0) return;
   const int row0 = p.offsets[e];
@@ -581,12 +580,13 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_prefill(GemmParams p) {
     if (sn < ntiles * 16) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const f16x2 sp = scale_pair_f16((ac.s >> (16 * (j >> 1))) & 0xFFFFu);
+        const f16x2 sp = j < 2 ? scale_pair_f16<false>(ac.s) : scale_pair_f16<true>(ac.s);
         const f16x2 s2 = (j & 1) ? __builtin_shufflevector(sp, sp, 1, 1) : __builtin_shufflevector(sp, sp, 0, 0);
-        const uint32_t wv4[4] = {ac.v[j].x, ac.v[j].y, ac.v[j].z, ac.v[j].w};
+        u32x4 u4[4];
+        act_group_kprime(ac.v[j], s2, u4);
 #pragma unroll
-        for (int h = 0; h < 4; ++h)                // 8-K chunk 4 (4 sh + j) + h of the step
-          *reinterpret_cast<u32x4*>(sB + sn * RS + (4 * (4 * sh + j) + h) * 16) = act_chunk_kprime(wv4[h], s2);
+        for (int h = 0; h < 4; ++h)                // LDS unit 4 (4 sh + j) + h of the step
+          *reinterpret_cast<u32x4*>(sB + sn * RS + (4 * (4 * sh + j) + h) * 16) = u4[h];
       }
     }
     __syncthreads();
@@ -608,7 +608,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_prefill(GemmParams p) {
         const f16x2 sp = scale_pair_f16(w.sc[rt]);
         const f16x2 s2 = (t < 2) ? __builtin_shufflevector(sp, sp, 0, 0) : __builtin_shufflevector(sp, sp, 1, 1);
         A[rt] = weight_operand_of<LAYOUT>(frag_word(w.pk[rt], t), s2);
-        idx[rt] = lut[(w.mk[rt] >> (8 * t)) & 255u];
+        idx[rt] = sparse_index<LAYOUT>(w.mk[rt], t, lut);
       }
       if (t == 3 && reload >= 0) {
         slot_decoded<4>(A, idx);

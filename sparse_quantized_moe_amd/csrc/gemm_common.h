@@ -92,7 +92,7 @@ struct WeightPtrs<1, RT> {
     for (int rt = 0; rt < RT; ++rt) {
       const int soff = tile_off[rt] + gs * kTileRecordBytes;
       w.pk[rt] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, l * 16u, soff, 0);
-      w.mk[rt] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, l * 4u + kTileMaskOffset, soff, 0);
+      w.mk[rt] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, l * 4u + kTileCodeOffset, soff, 0);
       w.sc[rt] = __builtin_amdgcn_raw_buffer_load_b16(rsrc, l * 2u + kTileScaleOffset, soff, 0);
     }
   }
@@ -113,6 +113,14 @@ __device__ __forceinline__ void slot_decoded(const f16x8 (&A)[RT], const int (&i
 template <int LAYOUT>
 __device__ __forceinline__ f16x8 weight_operand_of(uint32_t word, f16x2 s2) {
   return LAYOUT == 0 ? weight_operand(word, s2) : weight_operand_tiled(word, s2);
+}
+
+// Sparse-index word of smfmac t of a row-tile's fragment word mk: through the LDS table of mask
+// bytes (pair-bitmask layout) or by one byte permute of the record's code bytes (tiled layout).
+template <int LAYOUT>
+__device__ __forceinline__ int sparse_index(uint32_t mk, int t, const uint16_t* lut) {
+  if constexpr (LAYOUT == 1) return smfmac_index_of_codes(mk, t);
+  else return lut[(mk >> (8 * t)) & 255u];
 }
 
 __device__ __forceinline__ uint32_t frag_word(const u32x4& v, int t) {

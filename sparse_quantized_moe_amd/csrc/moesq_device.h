@@ -162,11 +162,10 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as
 // ---------------------------------------------------------------------------------------------
 // Operand decode for v_smfmac_f32_16x16x64_f16.
 //
-// K' order. Paired-4:8 keeps two of the four pairs of every 8-K chunk, so taking the even elements
-// of a chunk as one 4-group and the odd elements as the next gives exactly 2 kept elements per
-// 4-group, at the same positions (the kept pair ids i0 < i1) in both groups: the structured 2:4
-// pattern of the sparse MFMA. Activations are laid out in the same K' order
-// (e0 e2 e4 e6 | e1 e3 e5 e7 per chunk), which leaves every dot product unchanged.
+// K' order. Paired-4:8 keeps two of the four pairs of every 8-K chunk, so the even elements of a
+// chunk form a 4-group with exactly 2 kept elements, and so do its odd elements, at the same
+// positions (the kept pair ids i0 < i1) in both: the structured 2:4 pattern of the sparse MFMA. The
+// activations are laid out in the same K' order, which leaves every dot product unchanged.
 // ---------------------------------------------------------------------------------------------
 
 // Two fp4 codes of byte `sel` of w -> f16x2 (low nibble first), exact.
@@ -182,24 +181,35 @@ __device__ __forceinline__ f16x2 as_f16x2(uint32_t v) { return __builtin_bit_cas
 __device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
 __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
 
-// Dequantize the 8 codes of one activation chunk (one u32, low nibble = lower K) times scale s (f16)
-// into K' order: returns (e0 e2 | e4 e6 | e1 e3 | e5 e7) as 4 u32 of f16 pairs.
-__device__ __forceinline__ u32x4 act_chunk_kprime(uint32_t codes, f16x2 s2) {
-  const uint32_t d0 = as_u32(fp4x2_to_f16<0>(codes) * s2);
-  const uint32_t d1 = as_u32(fp4x2_to_f16<1>(codes) * s2);
-  const uint32_t d2 = as_u32(fp4x2_to_f16<2>(codes) * s2);
-  const uint32_t d3 = as_u32(fp4x2_to_f16<3>(codes) * s2);
-  u32x4 r;
-  r.x = pack_lo(d0, d1);
-  r.y = pack_lo(d2, d3);
-  r.z = pack_hi(d0, d1);
-  r.w = pack_hi(d2, d3);
-  return r;
+// Operand order of one smfmac (16 K of a lane = two adjacent 8-K chunks c, c+1, c even): the four
+// 4-groups of the 2:4 operand are (even K of c, even K of c+1, odd K of c, odd K of c+1). Both halves of a chunk
+// then share one 2-bit position pair, so the index word of the smfmac is the byte
+// code(c) | code(c+1) << 4 repeated in its two low bytes, code(q) = i0 | i1 << 2 for the nibble q
+// whose set bits are i0 < i1.
+//
+// Dense side: the B operand reads, per lane, 16-byte LDS units holding [even K of c | even K of c+1]
+// (unit c) and [odd K of c | odd K of c+1] (unit c+1) in f16.
+
+// Dequantize the 32 codes of one 32-K group (4 chunks, low nibble = lower K) times its scale s (f16
+// pair) into LDS units 0..3 of the group in B-operand order: u[2m] = even K of chunks 2m, 2m+1 and
+// u[2m+1] = their odd K (each 4 + 4 f16 values, ascending K).
+__device__ __forceinline__ void act_group_kprime(const u32x4& codes, f16x2 s2, u32x4 (&u)[4]) {
+  const uint32_t c[4] = {codes.x, codes.y, codes.z, codes.w};
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const uint32_t x = c[2 * m], y = c[2 * m + 1];
+    const uint32_t d0 = as_u32(fp4x2_to_f16<0>(x) * s2), d1 = as_u32(fp4x2_to_f16<1>(x) * s2);
+    const uint32_t d2 = as_u32(fp4x2_to_f16<2>(x) * s2), d3 = as_u32(fp4x2_to_f16<3>(x) * s2);
+    const uint32_t e0 = as_u32(fp4x2_to_f16<0>(y) * s2), e1 = as_u32(fp4x2_to_f16<1>(y) * s2);
+    const uint32_t e2 = as_u32(fp4x2_to_f16<2>(y) * s2), e3 = as_u32(fp4x2_to_f16<3>(y) * s2);
+    u[2 * m] = u32x4{pack_lo(d0, d1), pack_lo(d2, d3), pack_lo(e0, e1), pack_lo(e2, e3)};
+    u[2 * m + 1] = u32x4{pack_hi(d0, d1), pack_hi(d2, d3), pack_hi(e0, e1), pack_hi(e2, e3)};
+  }
 }
 
-// Compressed A operand of one smfmac from one u32 of kept bytes: bytes (b0 b1) of chunk 0 and
-// (b0' b1') of chunk 1. Slots 0,1 = (lo b0, lo b1) (evens of chunk 0), 2,3 = (hi b0, hi b1) (odds),
-// 4..7 the same for chunk 1, each times the block scale s (f16).
+// Compressed A operand of one smfmac from one u32 of kept bytes: bytes (b0 b1) of chunk c and
+// (b0' b1') of chunk c+1. Slots (lo b0, lo b1), (lo b0', lo b1'), (hi b0, hi b1), (hi b0', hi b1'),
+// each times the block scale s (f16).
 __device__ __forceinline__ f16x8 weight_operand(uint32_t kept, f16x2 s2) {
   const uint32_t c0 = as_u32(fp4x2_to_f16<0>(kept) * s2);
   const uint32_t c1 = as_u32(fp4x2_to_f16<1>(kept) * s2);
@@ -207,25 +217,25 @@ __device__ __forceinline__ f16x8 weight_operand(uint32_t kept, f16x2 s2) {
   const uint32_t c3 = as_u32(fp4x2_to_f16<3>(kept) * s2);
   u32x4 r;
   r.x = pack_lo(c0, c1);
-  r.y = pack_hi(c0, c1);
-  r.z = pack_lo(c2, c3);
+  r.y = pack_lo(c2, c3);
+  r.z = pack_hi(c0, c1);
   r.w = pack_hi(c2, c3);
   return __builtin_bit_cast(f16x8, r);
 }
 
 // Tiled layout: the 4 kept bytes (b0 b1)(b0' b1') of one smfmac rewritten as
-// (lo b0 | lo b1 << 4, hi b0 | hi b1 << 4, lo b0' | lo b1' << 4, hi b0' | hi b1' << 4), so byte j
+// (lo b0 | lo b1 << 4, lo b0' | lo b1' << 4, hi b0 | hi b1 << 4, hi b0' | hi b1' << 4), so byte j
 // converts straight to operand slots 2j, 2j+1.
 __host__ __device__ inline uint32_t kept_to_tiled(uint32_t w) {
   const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
   const uint32_t x = lo | (lo >> 4);          // byte0 = lo b0 | lo b1 << 4, byte2 = lo b0' | lo b1' << 4
   const uint32_t y = hi | (hi >> 4);          // byte0 = hi b0 | hi b1 << 4, byte2 = hi b0' | hi b1' << 4
-  return (x & 0xFFu) | ((y & 0xFFu) << 8) | (((x >> 16) & 0xFFu) << 16) | (((y >> 16) & 0xFFu) << 24);
+  return (x & 0xFFu) | (((x >> 16) & 0xFFu) << 8) | ((y & 0xFFu) << 16) | (((y >> 16) & 0xFFu) << 24);
 }
 __host__ __device__ inline uint32_t tiled_to_kept(uint32_t t) {
   uint32_t out = 0;
   for (int h = 0; h < 2; ++h) {                // h = 0: (b0 b1), h = 1: (b0' b1')
-    const uint32_t X = (t >> (16 * h)) & 0xFFu, Y = (t >> (16 * h + 8)) & 0xFFu;
+    const uint32_t X = (t >> (8 * h)) & 0xFFu, Y = (t >> (8 * h + 16)) & 0xFFu;
     const uint32_t b0 = (X & 15u) | ((Y & 15u) << 4), b1 = (X >> 4) | (Y & 0xF0u);
     out |= (b0 | (b1 << 8)) << (16 * h);
   }
@@ -242,35 +252,56 @@ __device__ __forceinline__ f16x8 weight_operand_tiled(uint32_t t, f16x2 s2) {
   return __builtin_bit_cast(f16x8, r);
 }
 
-// Sparse-index word of one smfmac from the mask byte of its two chunks: each chunk's nibble q (two
-// bits set, i0 < i1) gives the 4-bit code i0 | i1 << 2 for its even group and again for its odd group.
-__host__ __device__ inline uint32_t smfmac_index_of_mask_byte(uint32_t b) {
-  uint32_t out = 0;
-  for (int h = 0; h < 2; ++h) {
-    const uint32_t q = (b >> (4 * h)) & 15u;
-    uint32_t i0 = 0, i1 = 0, seen = 0;
-    for (uint32_t i = 0; i < 4; ++i)
-      if (q & (1u << i)) { if (seen == 0) i0 = i; else i1 = i; ++seen; }
-    const uint32_t code = i0 | (i1 << 2);
-    out |= (code | (code << 4)) << (8 * h);
-  }
-  return out;
+// Position code of a mask nibble: i0 | i1 << 2 for its lowest and highest set bits (the two kept
+// pairs of a valid nibble), and its inverse. Nibbles without exactly two bits set are outside the
+// format and do not survive the round trip.
+__host__ __device__ inline uint32_t nibble_code(uint32_t q) {
+  uint32_t i0 = 0, i1 = 0;
+  for (uint32_t i = 0; i < 4; ++i)
+    if (q & (1u << i)) i1 = i;
+  for (int i = 3; i >= 0; --i)
+    if (q & (1u << i)) i0 = (uint32_t)i;
+  return i0 | (i1 << 2);
+}
+__host__ __device__ inline uint32_t code_nibble(uint32_t c) { return (1u << (c & 3u)) | (1u << (c >> 2)); }
+
+// Code byte of a mask byte (its two chunks' nibbles, low nibble first) and back.
+__host__ __device__ inline uint32_t mask_to_code_byte(uint32_t b) {
+  return nibble_code(b & 15u) | (nibble_code((b >> 4) & 15u) << 4);
+}
+__host__ __device__ inline uint32_t code_to_mask_byte(uint32_t b) {
+  return code_nibble(b & 15u) | (code_nibble((b >> 4) & 15u) << 4);
 }
 
-// f16 value of a non-negative E4M3 scale byte (exact: E4M3 lies inside f16's range and precision).
-__device__ __forceinline__ f16 e4m3_to_f16(uint32_t b) { return (f16)e4m3_value(b); }
+// Sparse-index word of one smfmac from the mask byte of its two chunks (pair-bitmask layout, through
+// a 256-entry table) ...
+__host__ __device__ inline uint32_t smfmac_index_of_mask_byte(uint32_t b) {
+  const uint32_t y = mask_to_code_byte(b);
+  return y | (y << 8);
+}
 
-// Both E4M3 scale bytes of a u16 (low, high) as an f16 pair: the E4M3 magnitude bits shifted into
-// an f16 field are the value times 2^-8 (normals and subnormals alike), so one packed multiply by
-// 256 gives the exact pair. The sign bits are ignored (scales are non-negative).
-__device__ __forceinline__ f16x2 scale_pair_f16(uint32_t sc16) {
-  const uint32_t bits = ((sc16 & 0x7Fu) << 7) | ((sc16 & 0x7F00u) << 15);
-  return as_f16x2(bits) * f16x2{(f16)256.0f, (f16)256.0f};
+// ... and from byte t of a word of code bytes (tiled layout), with one byte permute.
+__device__ __forceinline__ int smfmac_index_of_codes(uint32_t codes, int t) {
+  return (int)__builtin_amdgcn_perm(codes, codes, 0x0C0C0000u | ((uint32_t)t << 8) | (uint32_t)t);
+}
+
+// E4M3 scale bytes 0 and 1 (HI: 2 and 3) of sc as an f16 pair, by the hardware FP8 (E4M3FN) to f16
+// conversion with unit scale: exact, since E4M3 lies inside f16's range and precision (checked for
+// all 256 bytes on gfx950). A broadcast of one half folds into the consumer's op_sel.
+template <bool HI = false>
+__device__ __forceinline__ f16x2 scale_pair_f16(uint32_t sc) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc, 1.0f, HI);
+}
+
+// f16 pair (v, v) of one E4M3 scale byte.
+__device__ __forceinline__ f16x2 scale_bcast_f16(uint32_t b) {
+  const f16x2 p = scale_pair_f16(b);
+  return __builtin_shufflevector(p, p, 0, 0);
 }
 
 // Tiled weight record: 1408 bytes per (expert, 16-row tile, 256-K step).
 constexpr int kTileRecordBytes = 1408;
-constexpr int kTileMaskOffset = 1024;
+constexpr int kTileCodeOffset = 1024;
 constexpr int kTileScaleOffset = 1280;
 
 // Word 3 of a raw buffer resource on gfx9-family targets (gfx950): no format conversion, no swizzle;

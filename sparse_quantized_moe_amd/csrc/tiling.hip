@@ -2,9 +2,11 @@
 //
 // The model cards ("Sparse storage layout") note that the serving stack rebuilds each layer into the
 // GEMM kernel's own layout at load time; here that layout keeps the same bytes, reordered so that one
-// 256-K step of a 16-row tile is one contiguous 1408-byte record (1024 B kept bytes, 256 B masks,
-// 128 B scales, each in lane order), and the kept-byte nibbles of each smfmac are pre-arranged into
-// operand order. A wave then reads each of its fragments with fully coalesced loads.
+// 256-K step of a 16-row tile is one contiguous 1408-byte record (1024 B kept bytes, 256 B index
+// codes, 128 B scales, each in lane order): the kept-byte nibbles of each smfmac are pre-arranged
+// into operand order, and each mask nibble is replaced by the position code of its two kept pairs,
+// which the kernels use as the sparse index with no table. A wave then reads each of its fragments
+// with fully coalesced loads.
 #include "moesq_device.h"
 #include "moesq_internal.h"
 
@@ -31,7 +33,9 @@ __global__ __launch_bounds__(256) void k_prepare(const uint8_t* __restrict__ pac
   u32x4 t;
   t.x = kept_to_tiled(pk.x); t.y = kept_to_tiled(pk.y); t.z = kept_to_tiled(pk.z); t.w = kept_to_tiled(pk.w);
   *reinterpret_cast<u32x4*>(r + 16 * lane) = t;
-  *reinterpret_cast<uint32_t*>(r + kTileMaskOffset + 4 * lane) = mk;
+  const uint32_t code = mask_to_code_byte(mk & 255u) | mask_to_code_byte((mk >> 8) & 255u) << 8 |
+                        mask_to_code_byte((mk >> 16) & 255u) << 16 | mask_to_code_byte(mk >> 24) << 24;
+  *reinterpret_cast<uint32_t*>(r + kTileCodeOffset + 4 * lane) = code;
   *reinterpret_cast<uint16_t*>(r + kTileScaleOffset + 2 * lane) = sc;
 }
 
@@ -53,7 +57,10 @@ __global__ __launch_bounds__(256) void k_unprepare(const uint8_t* __restrict__ t
   u32x4 pk;
   pk.x = tiled_to_kept(t.x); pk.y = tiled_to_kept(t.y); pk.z = tiled_to_kept(t.z); pk.w = tiled_to_kept(t.w);
   *reinterpret_cast<u32x4*>(packed + row * (K >> 2) + (k0 >> 2)) = pk;
-  *reinterpret_cast<uint32_t*>(mask + row * (K >> 4) + (k0 >> 4)) = *reinterpret_cast<const uint32_t*>(r + kTileMaskOffset + 4 * lane);
+  const uint32_t code = *reinterpret_cast<const uint32_t*>(r + kTileCodeOffset + 4 * lane);
+  *reinterpret_cast<uint32_t*>(mask + row * (K >> 4) + (k0 >> 4)) =
+      code_to_mask_byte(code & 255u) | code_to_mask_byte((code >> 8) & 255u) << 8 |
+      code_to_mask_byte((code >> 16) & 255u) << 16 | code_to_mask_byte(code >> 24) << 24;
   *reinterpret_cast<uint16_t*>(scale + row * (K >> 5) + (k0 >> 5)) = *reinterpret_cast<const uint16_t*>(r + kTileScaleOffset + 2 * lane);
 }
 

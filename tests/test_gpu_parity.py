@@ -223,11 +223,17 @@ def _tiled_reference(packed, mask, scale):
                         b = kb + 4 * t
                         rec = out[e, tile, ss]
                         rec[16 * lane + 4 * t + 0] = lo[e, row, b] | (lo[e, row, b + 1] << 4)
-                        rec[16 * lane + 4 * t + 1] = hi[e, row, b] | (hi[e, row, b + 1] << 4)
-                        rec[16 * lane + 4 * t + 2] = lo[e, row, b + 2] | (lo[e, row, b + 3] << 4)
+                        rec[16 * lane + 4 * t + 1] = lo[e, row, b + 2] | (lo[e, row, b + 3] << 4)
+                        rec[16 * lane + 4 * t + 2] = hi[e, row, b] | (hi[e, row, b + 1] << 4)
                         rec[16 * lane + 4 * t + 3] = hi[e, row, b + 2] | (hi[e, row, b + 3] << 4)
                     m0 = (ss * 256 + 64 * q) // 16
-                    out[e, tile, ss, 1024 + 4 * lane: 1028 + 4 * lane] = mask[e, row, m0:m0 + 4]
+                    for j in range(4):                               # mask byte -> two position codes
+                        mb = int(mask[e, row, m0 + j])
+                        codes = []
+                        for nib in (mb & 15, mb >> 4):
+                            bits = [i for i in range(4) if nib >> i & 1]
+                            codes.append(bits[0] | (bits[-1] << 2))
+                        out[e, tile, ss, 1024 + 4 * lane + j] = codes[0] | (codes[1] << 4)
                     s0 = (ss * 256 + 64 * q) // 32
                     out[e, tile, ss, 1280 + 2 * lane: 1282 + 2 * lane] = scale[e, row, s0:s0 + 2]
     return out.reshape(-1)
