@@ -153,8 +153,10 @@ def run_steps(moesq, torch, ev, x, ids_t, wts_t, layers, g13_t, g2_t, out, ws, w
 
 def measured_peaks(moesq, torch, ev):
     """What this GPU sustains, beside the published peaks: a plain 1 GiB device copy (read + write
-    bytes per second) and the library's probe of v_smfmac_f32_16x16x64_f16 (kept-half FLOP/s: 16384
-    per instruction), both timed with HIP events on the current stream."""
+    bytes per second), the library's read-stream probe over the same 1 GiB (the ceiling of kernels
+    that read much and write little, as the decode GEMMs do) and its probe of
+    v_smfmac_f32_16x16x64_f16 (kept-half FLOP/s: 16384 per instruction), all timed with HIP events
+    on the current stream."""
     n = 1 << 30
     src = torch.ones(n, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
@@ -167,6 +169,15 @@ def measured_peaks(moesq, torch, ev):
     ev.record(e[1])
     torch.cuda.synchronize()
     copy_gbs = 2 * n * 5 / (ev.elapsed_ms(e[0], e[1]) * 1e-3) / 1e9
+    word = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        moesq.probe_read(src, word)
+    ev.record(e[0])
+    for _ in range(5):
+        moesq.probe_read(src, word)
+    ev.record(e[1])
+    torch.cuda.synchronize()
+    read_gbs = n * 5 / (ev.elapsed_ms(e[0], e[1]) * 1e-3) / 1e9
     del src, dst
     blocks = 2 * torch.cuda.get_device_properties(0).multi_processor_count
     sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
@@ -177,7 +188,7 @@ def measured_peaks(moesq, torch, ev):
     torch.cuda.synchronize()
     tf = insts * 16384 / (ev.elapsed_ms(e[0], e[1]) * 1e-3) / 1e12
     ev.destroy(e)
-    return {"copy_GBps": round(copy_gbs, 1), "smfmac_f16_kept_TFLOPs": round(tf, 1)}
+    return {"copy_GBps": round(copy_gbs, 1), "read_GBps": round(read_gbs, 1), "smfmac_f16_kept_TFLOPs": round(tf, 1)}
 
 
 def router_figures(moesq, torch, ev, reps=50):
@@ -385,7 +396,7 @@ def main():
         log(f"copy calibration: 3 copies of {n} bytes")
         del src, dst
     peaks = measured_peaks(moesq, torch, ev)
-    log(f"measured: device copy {peaks['copy_GBps']} GB/s, smfmac f16 {peaks['smfmac_f16_kept_TFLOPs']} TFLOP/s (kept half)")
+    log(f"measured: device copy {peaks['copy_GBps']} GB/s, read stream {peaks['read_GBps']} GB/s, smfmac f16 {peaks['smfmac_f16_kept_TFLOPs']} TFLOP/s (kept half)")
     wl = synth.WORKLOADS[args.workload]
     w13, w2, dense_expert = build_layer(wl, args.seed, dev)
     layers = [(w13, w2)]
@@ -469,7 +480,8 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": kbytes,
                      "avg_launch_us": round(k_ms * 1e3, 2),
-                     "measured_peak": peaks["copy_GBps"], "frac_of_measured": round(achieved / peaks["copy_GBps"], 4)},
+                     "measured_peak": peaks["read_GBps"], "measured_peak_kind": "read stream (library probe)",
+                     "frac_of_measured": round(achieved / peaks["read_GBps"], 4)},
         "measured_peaks": peaks,
         "side_passes": None if fused else side_passes(wl, P, float(st_mean[len(moesq.FFN_STAGES)]),
                                                       float(st_mean[len(moesq.FFN_STAGES) + 3])),

@@ -206,6 +206,12 @@ moesq_status moesq_set_stage_events(hipEvent_t *events /* host */, int32_t n);
 moesq_status moesq_probe_smfmac(int32_t blocks, int32_t iters, float *sink, int64_t *n_insts /* host */,
                                 hipStream_t stream);
 
+/* Measurement aid: a read stream of `bytes` bytes from src (device, 16-byte aligned, bytes a positive
+ * multiple of 16) with 16-byte loads over the whole GPU, the ceiling of kernels that read much and
+ * write little; time it with events on `stream`. sink: one uint32 (device), written only if the
+ * data's fold equals a fixed constant. */
+moesq_status moesq_probe_read(const void *src, int64_t bytes, uint32_t *sink, hipStream_t stream);
+
 /* Weight compression of a dense fp32 linear [N][K] into pair-bitmask NVFP4 (the synthetic-layer
  * recipe; model card "Compression details": paired 4:8 along K, 2 of every 4 pairs kept): in each
  * 8-K chunk keep the 2 pairs with the largest a*a + b*b (float64, ties to the lower pair),

@@ -37,7 +37,7 @@ EXPORTED_SYMBOLS = (
     "moesq_grouped_gemm_workspace_size", "moesq_grouped_gemm", "moesq_moe_ffn_layout",
     "moesq_moe_ffn_workspace_size", "moesq_moe_ffn", "moesq_compress_weights", "moesq_validate_weights",
     "moesq_unpack_pair_bitmask", "moesq_pack_pair_bitmask", "moesq_set_stage_events", "moesq_tiled_bytes",
-    "moesq_prepare_weights", "moesq_unprepare_weights", "moesq_permute_workspace_size", "moesq_probe_smfmac",
+    "moesq_prepare_weights", "moesq_unprepare_weights", "moesq_permute_workspace_size", "moesq_probe_smfmac", "moesq_probe_read",
     "moesq_route_topk", "moesq_fold_gate_up_globals",
 )
 
@@ -87,6 +87,7 @@ def _declare(L: ctypes.CDLL) -> None:
         "moesq_pack_pair_bitmask": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _P, _P]),
         "moesq_set_stage_events": (ctypes.c_int, [_P, _I32]),
         "moesq_probe_smfmac": (ctypes.c_int, [_I32, _I32, _P, ctypes.POINTER(_I64), _P]),
+        "moesq_probe_read": (ctypes.c_int, [_P, _I64, _P, _P]),
         "moesq_route_topk": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I32, _I32, _I32, _P, _P, _P]),
         "moesq_tiled_bytes": (_SZ, [_I32, _I32, _I32]),
         "moesq_fold_gate_up_globals": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P]),
@@ -378,7 +379,7 @@ def set_stage_events(events) -> None:
         _check(lib().moesq_set_stage_events(ctypes.cast(events, ctypes.c_void_p), len(events)))
 
 
-__all__ += ["FFN_STAGES", "set_stage_events", "probe_smfmac", "route_topk"]
+__all__ += ["FFN_STAGES", "set_stage_events", "probe_smfmac", "probe_read", "route_topk"]
 
 
 def route_topk(logits: torch.Tensor, k: int, renormalize: bool = True, out_ids: Optional[torch.Tensor] = None,
@@ -406,6 +407,16 @@ def probe_smfmac(blocks: int, iters: int, sink: torch.Tensor) -> int:
     _check(lib().moesq_probe_smfmac(blocks, iters, _dev(sink, "sink", torch.float32), ctypes.byref(n),
                                     _stream()))
     return n.value
+
+
+def probe_read(src: torch.Tensor, sink: torch.Tensor) -> int:
+    """Launch the HBM read-stream probe over all of src (contiguous, 16-byte multiple) on the current
+    stream (see moesq_probe_read); returns the bytes read. sink: >= 1 int32 on device."""
+    nbytes = src.numel() * src.element_size()
+    if sink.numel() < 1:
+        raise MoesqError("probe_read: sink too small")
+    _check(lib().moesq_probe_read(_dev(src, "src"), nbytes, _dev(sink, "sink", torch.int32), _stream()))
+    return nbytes
 
 
 def validate_weights(mask: torch.Tensor, K: int) -> int:

@@ -122,6 +122,14 @@ moesq_status moesq_probe_smfmac(int32_t blocks, int32_t iters, float* sink, int6
   return check_launch(stream, false);
 }
 
+moesq_status moesq_probe_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream) {
+  MOESQ_REQUIRE(src && sink && bytes >= 16 && bytes % 16 == 0, MOESQ_ERR_INVALID,
+                "probe_read: src and sink required, bytes a positive multiple of 16");
+  MOESQ_REQUIRE((reinterpret_cast<uintptr_t>(src) & 15u) == 0, MOESQ_ERR_INVALID, "probe_read: src must be 16-byte aligned");
+  moesq::launch_probe_read(src, bytes, sink, stream);
+  return check_launch(stream, false);
+}
+
 moesq_status moesq_quantize_act(const void* x, moesq_dtype x_dtype, int64_t rows, int32_t K, int64_t x_row_stride,
                                 const int32_t* src_row, const int32_t* expert_offsets, int32_t E, const float* global,
                                 uint8_t* codes, uint8_t* scales, hipStream_t stream) {

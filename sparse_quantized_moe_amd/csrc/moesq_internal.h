@@ -114,6 +114,7 @@ void launch_route_topk(const void* logits, bool f32, int64_t T, int E, int k, bo
 
 // smfmac throughput probe (probe.hip): returns the number of instructions the launch issues.
 int64_t launch_probe_smfmac(int blocks, int iters, float* sink, hipStream_t stream);
+void launch_probe_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
 
 // out[t][:] = sum_j D[inv[t*k + j]][:] (rows with inv < 0 skipped), in j order.
 void launch_combine(const float* D, const int* inv, int64_t T, int k, int H, float* out, hipStream_t stream);

@@ -106,6 +106,12 @@ def test_argument_checks_return_status_without_launching():
     assert L.moesq_fold_gate_up_globals(P, P, 4, 64, 48, None) == INVALID
     assert L.moesq_fold_gate_up_globals(None, P, 4, 64, 256, None) == INVALID
     assert L.moesq_fold_gate_up_globals(None, None, 0, 64, 256, None) == OK
+    # probes: bad sizes, null or misaligned pointers
+    assert L.moesq_probe_read(P, 0, P, None) == INVALID
+    assert L.moesq_probe_read(P, 40, P, None) == INVALID
+    assert L.moesq_probe_read(None, 64, P, None) == INVALID
+    assert L.moesq_probe_read(ctypes.c_void_p(24), 64, P, None) == INVALID
+    assert L.moesq_probe_smfmac(0, 4, P, ctypes.byref(ctypes.c_int64()), None) == INVALID
     # compress and codec
     assert L.moesq_compress_weights(P, 4, 40, P, P, P, P, None) == INVALID
     assert L.moesq_validate_weights(P, 4, 40, P, None) == INVALID

@@ -487,6 +487,16 @@ def test_stage_events_time_the_kernels(flags):
         ev.destroy(evs)
 
 
+def test_probe_read_returns_bytes_and_keeps_sink():
+    """The read probe reads all of src (1 MiB of ones: every thread's fold is 0, not the constant that
+    triggers the store) and leaves the sink alone."""
+    src = torch.ones(1 << 20, dtype=torch.uint8, device=DEV)
+    sink = torch.full((1,), 7, dtype=torch.int32, device=DEV)
+    assert moesq.probe_read(src, sink) == 1 << 20
+    torch.cuda.synchronize()
+    assert sink.item() == 7
+
+
 def test_probe_smfmac_counts_and_writes():
     """The MFMA throughput probe issues blocks x 4 waves x iters x 32 instructions and writes its sink."""
     sink = torch.full((4 * 256,), float("nan"), dtype=torch.float32, device=DEV)
