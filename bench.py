@@ -541,10 +541,16 @@ def main():
 
 
 def _kernel_sha(files) -> str:
+    """Hash of the kernel sources' code: comments and whitespace runs are dropped first, so an edit
+    of the comments alone keeps a traffic figure taken on the same code."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in files:
-        h.update(open(os.path.join(ROOT, "sparse_quantized_moe_amd", "csrc", f), "rb").read())
+        text = open(os.path.join(ROOT, "sparse_quantized_moe_amd", "csrc", f)).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

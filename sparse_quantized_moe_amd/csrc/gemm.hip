@@ -15,15 +15,19 @@
 // fp32 epilogue.
 //
 // Lane data per 256-K super-step: lane (row = lane % 16, q = lane / 16) of a row-tile holds the 64
-// contiguous K [64 q, 64 q + 64) of its weight row (16 B kept bytes, 4 B masks, 2 B scales; one load
-// each), and smfmac t (t = 0..3) uses chunks 2t, 2t+1 of it. The sparse operand's lane q covers the
+// contiguous K [64 q, 64 q + 64) of its weight row (16 B kept bytes, 4 B masks or index codes, 2 B
+// scales; one load each), and smfmac t (t = 0..3) uses chunks 2t, 2t+1 of it. The sparse operand's lane q covers the
 // MFMA's 8-K chunk positions {c0(q), c0(q) + 2} with c0 = 0, 4, 1, 5 for q = 0..3, so B lane qb must
 // hold the local chunks 8*(qb/2) + 2t + (qb%2) and that + 16.
 //
-// Two kernels:
-//   * k_gemm_decode (small batches): a workgroup owns one m-block (<= 32 rows of one expert) and
-//     256 weight rows; its activations are staged in LDS as exact f16 in the B-operand order (32 KB
-//     at a time). Weights stream from HBM straight into registers, two super-steps ahead.
+// Kernels:
+//   * k_gemm_decode (small batches, any K): a workgroup owns one m-block (<= 32 rows of one expert)
+//     and one n-block of weight rows; its activations are staged in LDS as exact f16 in the B-operand
+//     order, 512 K at a time. Weights stream from HBM straight into registers, a few super-steps ahead.
+//   * k_gemm_decode_nloop (small batches, K <= 1024, not gate/up): the whole K staged once; a
+//     workgroup walks several n-blocks with its weight ring running across their boundaries.
+//   * k_gemm_decode_stream (small batches, gate/up, tiled weights, K <= 2048): the whole K staged once
+//     for 12 waves that each stream 32 intermediate columns.
 //   * k_gemm_prefill (large batches): a workgroup owns 128 rows x 256 weight rows; per 256-K step it
 //     dequantizes the activations into LDS as f16 and each wave reuses every decoded weight fragment
 //     over 8 token tiles.

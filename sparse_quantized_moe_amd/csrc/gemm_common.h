@@ -6,8 +6,9 @@
 
 namespace moesq {
 
-// Kept bytes, masks and scales one lane needs for one 256-K super-step of 4 row-tiles: 16 B of
-// packed, 4 B of mask and 2 B of scale per row-tile (the lane's 64 contiguous K of its row).
+// Kept bytes, masks (tiled layout: index codes) and scales one lane needs for one 256-K super-step
+// of RT row-tiles: 16 B of packed, 4 B of mask and 2 B of scale per row-tile (the lane's 64
+// contiguous K of its row).
 template <int RT = 4>
 struct WeightFrag {
   u32x4 pk[RT];
