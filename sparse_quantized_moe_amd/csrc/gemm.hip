@@ -507,15 +507,32 @@ constexpr int kPreLdsB = kPreBMT * kPreRowStride;
 // one expert (same weights) run side by side on one L2 instead of being fetched by every XCD.
 constexpr int kXcds = 8;
 
-// A workgroup owns one m-block (<= 128 rows of one expert) and 256 weight rows; each wave keeps 4
+// Waves per prefill workgroup (each 4 row-tiles of 16 weight rows) and the n-blocks they make. The
+// gate/up GEMM on tiled weights runs 8 waves (512 weight rows, one workgroup per CU): each staged
+// activation step then feeds twice the weight rows, which took its time from 290 to 283 us on the
+// 128-expert layer and from 513 to 486 us on the 512-expert layer. The down GEMM was 4-5 % slower
+// that way and keeps 4 waves (two workgroups per CU); so does the pair-bitmask layout, whose larger
+// register set would spill at 8.
+template <int EPI, int LAYOUT>
+__host__ __device__ constexpr int prefill_waves() { return EPI == kEpiGateUp && LAYOUT == 1 ? 8 : 4; }
+
+template <int EPI, int NWP>
+__host__ __device__ constexpr int prefill_nblocks(int N) {
+  return EPI == kEpiGateUp ? ((N >> 1) + 32 * NWP - 1) / (32 * NWP) : (N + 64 * NWP - 1) / (64 * NWP);
+}
+
+// A workgroup owns one m-block (<= 128 rows of one expert) and 64 NWP weight rows; each wave keeps 4
 // row-tiles x 8 token tiles of accumulators and reuses every decoded weight fragment over the 8
 // token tiles. Per 256-K step the activations are converted to exact f16 in LDS; their codes are
-// prefetched into registers one step ahead (two threads per row, 64 B of codes + 4 scale bytes
-// each), and the weights run through a two-slot register ring reloaded right after decode, so every
-// global load in the K loop is a prefetch issued on every path.
-template <int EPI, int LAYOUT>
-__global__ __launch_bounds__(kGemmThreads) void k_gemm_prefill(GemmParams p) {
+// prefetched into registers one step ahead (NWP / 2 threads per row, each 256 / NWP bytes of codes
+// and 16 / NWP scale bytes), and the weights run through a two-slot register ring reloaded right
+// after decode, so every global load in the K loop is a prefetch issued on every path.
+template <int EPI, int LAYOUT, int NWP>
+__global__ __launch_bounds__(NWP * 64) void k_gemm_prefill(GemmParams p) {
   constexpr int TG = kPreTG, BMT = kPreBMT, RS = kPreRowStride;
+  constexpr int SPR = NWP * 64 / BMT;              // staging threads per row
+  constexpr int GPT = 8 / SPR;                     // 32-K groups per staging thread and step
+  static_assert(SPR * BMT == NWP * 64 && (GPT == 4 || GPT == 2), "staging map");
   extern __shared__ __align__(16) uint8_t smem[];
   uint8_t* sB = smem;                              // [BMT][RS] f16 of one 256-K step
   uint16_t* lut = reinterpret_cast<uint16_t*>(smem + kPreLdsB);
@@ -525,14 +542,14 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_prefill(GemmParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int K = p.K;
-  const int nblocks = EPI == kEpiGateUp ? ((p.N >> 1) + 127) / 128 : (p.N + 255) / 256;
+  const int nblocks = prefill_nblocks<EPI, NWP>(p.N);
   const int items = p.tile_offsets[p.E] * nblocks;
   const int per = (items + kXcds - 1) / kXcds;
   const int xi = (int)(blockIdx.x / kXcds);
   const int w_item = (int)(blockIdx.x % kXcds) * per + xi;
   if (xi >= per || w_item >= items) return;
   const int mb = w_item / nblocks, nb = w_item - mb * nblocks;
-  if (LAYOUT == 0) lut[tid] = (uint16_t)smfmac_index_of_mask_byte((uint32_t)tid);
+  if (LAYOUT == 0 && tid < 256) lut[tid] = (uint16_t)smfmac_index_of_mask_byte((uint32_t)tid);
   const int e = find_expert(p.tile_offsets, p.E, mb, &s_e);
   if (e < 0) return;
   const int row0 = p.offsets[e];
@@ -554,7 +571,8 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_prefill(GemmParams p) {
   const EpiScalars es = epi_scalars<EPI>(p, e);
 
   int wrow[4];
-  const bool active = wave_rows<EPI>(p.N, nb, wv, wrow);
+  const int gw = nb * NWP + wv;                    // wave index over the expert's weight rows
+  const bool active = wave_rows<EPI>(p.N, 0, gw, wrow);
   WeightPtrs<LAYOUT> wp;
   wp.init(p, e, wrow, active, lane);
   const int nsteps = K >> 8;
@@ -563,34 +581,36 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_prefill(GemmParams p) {
       const_cast<uint8_t*>(p.a_codes), (short)0, (int)(p.rows * (K >> 1)), kBufferRsrcWord3);
   const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(p.a_scales), (short)0, (int)(p.rows * (K >> 5)), kBufferRsrcWord3);
-  // staging map: thread -> row sn, 32-K groups 4 h .. 4 h + 3 of each step; consecutive lanes take
-  // consecutive rows, so each 8-lane LDS write group lands on 8 rows (different banks via the skew)
+  // staging map: thread -> row sn, 32-K groups GPT sh .. GPT sh + GPT - 1 of each step; consecutive
+  // lanes take consecutive rows, so each 8-lane LDS write group lands on 8 rows (different banks via
+  // the skew)
   const int sn = tid % BMT, sh = tid / BMT;
   __syncthreads();                                 // s_arow
   const bool srow_live = sn < mrows;
   const uint32_t ar = (uint32_t)s_arow[srow_live ? sn : 0];
-  struct Act { u32x4 v[4]; uint32_t s; };
+  struct Act { u32x4 v[GPT]; uint32_t s; };
   auto prefetch = [&](int gs, Act& ac) {
     const bool live = srow_live && gs < nsteps;
-    const uint32_t cb = ar * (uint32_t)(K >> 1) + (uint32_t)(gs * 128 + sh * 64);
+    const uint32_t cb = ar * (uint32_t)(K >> 1) + (uint32_t)(gs * 128 + sh * 16 * GPT);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < GPT; ++j)
       ac.v[j] = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, live ? cb + 16u * j : kOutOfRange, 0, 0);
-    ac.s = __builtin_amdgcn_raw_buffer_load_b32(
-        s_rsrc, live ? ar * (uint32_t)(K >> 5) + (uint32_t)(gs * 8 + sh * 4) : kOutOfRange, 0, 0);
+    const uint32_t so = live ? ar * (uint32_t)(K >> 5) + (uint32_t)(gs * 8 + sh * GPT) : kOutOfRange;
+    if constexpr (GPT == 4) ac.s = __builtin_amdgcn_raw_buffer_load_b32(s_rsrc, so, 0, 0);
+    else ac.s = __builtin_amdgcn_raw_buffer_load_b16(s_rsrc, so, 0, 0);
   };
   auto commit = [&](const Act& ac) {
     __syncthreads();
     if (sn < ntiles * 16) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < GPT; ++j) {
         const f16x2 sp = j < 2 ? scale_pair_f16<false>(ac.s) : scale_pair_f16<true>(ac.s);
         const f16x2 s2 = (j & 1) ? __builtin_shufflevector(sp, sp, 1, 1) : __builtin_shufflevector(sp, sp, 0, 0);
         u32x4 u4[4];
         act_group_kprime(ac.v[j], s2, u4);
 #pragma unroll
-        for (int h = 0; h < 4; ++h)                // LDS unit 4 (4 sh + j) + h of the step
-          *reinterpret_cast<u32x4*>(sB + sn * RS + (4 * (4 * sh + j) + h) * 16) = u4[h];
+        for (int h = 0; h < 4; ++h)                // LDS unit 4 (GPT sh + j) + h of the step
+          *reinterpret_cast<u32x4*>(sB + sn * RS + (4 * (GPT * sh + j) + h) * 16) = u4[h];
       }
     }
     __syncthreads();
@@ -663,7 +683,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_prefill(GemmParams p) {
     __syncthreads();
   }
   if (!active) return;
-  gemm_epilogue<EPI, TG>(p, es, acc, row0, m0, mrows, nb, wv, wrow, s_rw, lane);
+  gemm_epilogue<EPI, TG>(p, es, acc, row0, m0, mrows, 0, gw, wrow, s_rw, lane);
 }
 
 KernelEvents& kernel_events() {
@@ -741,13 +761,14 @@ static void launch_decode(const GemmParams& p, hipStream_t stream) {
 template <int EPI, int LAYOUT>
 static void launch_prefill(const GemmParams& p, hipStream_t stream) {
   const size_t lds = gemm_lds_bytes(kTacticPrefill, p.K);
-  set_lds_attr(&k_gemm_prefill<EPI, LAYOUT>, lds);
+  constexpr int NWP = prefill_waves<EPI, LAYOUT>();
+  set_lds_attr(&k_gemm_prefill<EPI, LAYOUT, NWP>, lds);
   // an upper bound of the live m-blocks (each expert adds at most one partial m-block); the kernel
   // spreads the live items over the XCDs and the rest of the grid exits
   const int64_t mblocks = (p.rows + kPreBMT - 1) / kPreBMT + p.E;
-  const int nblocks = EPI == kEpiGateUp ? ((p.N >> 1) + 127) / 128 : (p.N + 255) / 256;
+  const int nblocks = prefill_nblocks<EPI, NWP>(p.N);
   const int64_t grid = ((mblocks * nblocks + kXcds - 1) / kXcds) * kXcds;
-  launch_kernel(k_gemm_prefill<EPI, LAYOUT>, dim3((unsigned)grid), dim3(kGemmThreads), lds, stream, p);
+  launch_kernel(k_gemm_prefill<EPI, LAYOUT, NWP>, dim3((unsigned)grid), dim3(NWP * 64), lds, stream, p);
 }
 
 template <int EPI>
