@@ -343,7 +343,9 @@ def _run_ffn(x, ids, wts, w13, w2, g13, g2):
                                                     (8, 512, 256, 64, 4, False, False),    # stored layout
                                                     (8, 512, 256, 512, 4, False, True),    # prefill tactic
                                                     (8, 512, 256, 512, 4, False, False),
-                                                    (6, 256, 512, 40, 3, True, True)])     # 1/2688 globals
+                                                    (6, 256, 512, 40, 3, True, True),      # 1/2688 globals
+                                                    (6, 768, 256, 384, 4, False, True),    # prefill, 3 gate/up steps
+                                                    (4, 1280, 512, 256, 2, False, True)])  # prefill, 5 gate/up steps
 def test_moe_ffn_small(E, H, I, T, k, fixed, tiled):
     from ffn_check import compare_ffn, oracle_layer
     w13, w2, dense_expert = _layer(21, E, H, I, tiled)
