@@ -458,12 +458,7 @@ def main():
         k_ms = float(st_mean[len(moesq.FFN_STAGES) + 1])   # the gate/up kernel, its own start/end events
         tname, tsrc = "traffic_gemm_gate_up_qwen3_30b_decode.json", ("gemm.hip", "gemm_common.h", "moesq_device.h")
     achieved = kbytes / (k_ms * 1e-3) / 1e9
-    traffic = None
-    tfile = os.path.join(ROOT, "profiles", tname)
-    if os.path.exists(tfile):
-        t = json.load(open(tfile))
-        if t.get("kernel_source_sha") == _kernel_sha(tsrc):
-            traffic = t.get("bytes_per_launch")
+    traffic = _traffic(tname, tsrc)
     result = {
         "metric": "MoE FFN effective dense TFLOP/s (prefill) + weight-stream GB/s (decode), 1 GPU",
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -522,7 +517,8 @@ def main():
                                        float(pst_mean[len(moesq.FFN_STAGES) + 3])),
             "roofline": {"bound": "mfma", "kernel": "k_gemm_prefill<gate_up>",
                          "achieved": round(ach, 2), "peak": F16_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(ach / F16_DENSE_PEAK_TFLOPS, 4), "traffic": None,
+                         "frac": round(ach / F16_DENSE_PEAK_TFLOPS, 4),
+                         "traffic": _traffic(f"traffic_gemm_gate_up_{pw.name}.json", ("gemm.hip", "gemm_common.h", "moesq_device.h")),
                          "algorithmic_flops_per_launch": alg_flops, "avg_launch_ms": round(g_ms, 4),
                          "measured_peak": peaks["smfmac_f16_kept_TFLOPs"],
                          "frac_of_measured": round(ach / peaks["smfmac_f16_kept_TFLOPs"], 4)},
@@ -538,6 +534,16 @@ def main():
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
+
+
+def _traffic(name, sources):
+    """HBM bytes per launch from a committed counter summary in profiles/, or None when there is none
+    or the kernel code has changed since the counters were taken."""
+    tfile = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(tfile):
+        return None
+    t = json.load(open(tfile))
+    return t.get("bytes_per_launch") if t.get("kernel_source_sha") == _kernel_sha(sources) else None
 
 
 def _kernel_sha(files) -> str:
