@@ -26,6 +26,8 @@
 // that makes every other workgroup leave too, and reports -1 in status[0].
 #include <unistd.h>
 
+#include <atomic>
+
 #include "gemm_common.h"
 
 namespace moesq {
@@ -600,12 +602,12 @@ bool fused_applicable(int64_t T, int H, int I, int k, int E) {
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return false;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
-  static size_t granted = 0;
-  if (lds > granted) {
+  static std::atomic<size_t> granted{0};   // always the same (largest) size, so racing first calls agree
+  if (lds > granted.load(std::memory_order_relaxed)) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_ffn_fused), hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)fused_lds_bytes(kFzMaxK, kFzMaxK, kFzMaxPairs)) != hipSuccess)
       return false;
-    granted = fused_lds_bytes(kFzMaxK, kFzMaxK, kFzMaxPairs);
+    granted.store(fused_lds_bytes(kFzMaxK, kFzMaxK, kFzMaxPairs), std::memory_order_relaxed);
   }
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&k_ffn_fused), kFzThreads,
                                                    lds) != hipSuccess)
@@ -615,9 +617,9 @@ bool fused_applicable(int64_t T, int H, int I, int k, int E) {
 }
 
 hipError_t launch_ffn_fused(const FusedLaunch& f, hipStream_t stream) {
-  static unsigned ticket = 0;
-  if (ticket == 0) ticket = (unsigned)(0x9E3779B9u * (unsigned)getpid()) | 1u;
-  ticket = ticket + 2u == 0u ? 1u : ticket + 2u;                   // odd, never zero
+  // launch tickets: odd (so never zero), distinct per launch of this process, seeded by the process id
+  static std::atomic<unsigned> next_ticket{(unsigned)(0x9E3779B9u * (unsigned)getpid()) | 1u};
+  const unsigned ticket = next_ticket.fetch_add(2u, std::memory_order_relaxed);
   FusedArgs a{};
   a.x = f.x; a.ids = f.ids; a.topk_weights = f.topk_weights; a.a13_global = f.a13_global; a.a2_global = f.a2_global;
   a.w13 = f.w13; a.w13_global = f.w13_global; a.w2 = f.w2; a.w2_global = f.w2_global;

@@ -31,6 +31,8 @@
 //   * k_gemm_prefill (large batches): a workgroup owns 128 rows x 256 weight rows; per 256-K step it
 //     dequantizes the activations into LDS as f16 and each wave reuses every decoded weight fragment
 //     over 8 token tiles.
+#include <atomic>
+
 #include "gemm_common.h"
 
 namespace moesq {
@@ -699,12 +701,13 @@ size_t gemm_lds_bytes(int tactic, int K) {
   return tactic == kTacticPrefill ? (size_t)kPreLdsB + 512 : DecGeom<3>::lds;
 }
 
+// Every caller passes the same size for a given kernel, so concurrent first calls set the same value.
 template <class Kern>
 static void set_lds_attr(Kern* k, size_t lds) {
-  static size_t done = 0;   // largest size already granted for this kernel
-  if (lds > done) {
+  static std::atomic<size_t> done{0};   // largest size already granted for this kernel
+  if (lds > done.load(std::memory_order_relaxed)) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    done = lds;
+    done.store(lds, std::memory_order_relaxed);
   }
 }
 

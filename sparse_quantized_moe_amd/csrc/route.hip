@@ -18,6 +18,8 @@
 // so it does not wait for the permutation; the GEMM reads row sorted[r] for its r-th row. A thread
 // loads one 32-group of a token once, takes its amax once and encodes it for a run of that token's
 // experts.
+#include <mutex>
+
 #include "moesq_device.h"
 #include "moesq_internal.h"
 
@@ -380,13 +382,12 @@ static size_t route_lds_bytes(int E) {
 void launch_route(const int* ids, int64_t T, int k, int E, int* counts, int* offsets, int* tile_offsets, int bm,
                   int* sorted, int* inv, int* status, void* scratch, const uint16_t* x, int H, const float* a_global,
                   uint8_t* codes, uint8_t* scales, hipStream_t stream) {
-  static bool attr = false;
-  if (!attr) {
+  static std::once_flag attr;
+  std::call_once(attr, [] {
     for (const void* f : {reinterpret_cast<const void*>(&k_route<8>), reinterpret_cast<const void*>(&k_route<16>),
                           reinterpret_cast<const void*>(&k_route<32>)})
       (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)route_lds_bytes(1024));
-    attr = true;
-  }
+  });
   RouteArgs a{};
   a.ids = ids; a.T = T; a.k = k; a.E = E;
   a.ntiles = T > 0 ? (int)((T + kRouteThreads - 1) / kRouteThreads) : 1;
