@@ -477,9 +477,10 @@ def test_stage_events_time_the_kernels(flags):
         fused = moesq.ffn_layout(T, H, I, k, E, flags)["fused"] == 1
         if fused:
             # one kernel: its pair lies inside the whole call; the other pairs are back-to-back event
-            # records after it, as short as the (empty) stage intervals that follow the kernel
+            # records after it, empty intervals like the stage intervals that follow the kernel (up
+            # to a few microseconds of event-record jitter) and far shorter than the kernel
             assert 0.0 < kern[0] <= sum(stage) + 1e-3, (stage, kern)
-            assert all(t <= max(stage[1:]) + 1e-3 for t in kern[1:]), (stage, kern)
+            assert all(t <= max(stage[1:]) + 5e-3 and t < 0.5 * kern[0] for t in kern[1:]), (stage, kern)
         else:
             for s_ms, k_ms in zip(stage, kern):
                 assert 0.0 < k_ms <= s_ms + 1e-3, (stage, kern)
