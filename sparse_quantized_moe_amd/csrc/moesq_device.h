@@ -146,6 +146,48 @@ __device__ __forceinline__ uint32_t nvfp4_codes(const float* x, float s, float g
   return w;
 }
 
+// Exact codes with one sign test per value and no branch on the data, for inputs with few significant
+// bits (bf16), where nvfp4_codes() would fall back in nearly every wave. With inv4 = 4 rcp(s g),
+// v4 = rint(|x| inv4) puts the quotient q = |x| / (s g) on a nearest multiple V = v4 / 4 of 1/4 (the
+// product is within a few ulps of 4q), and d = fma(-(v4 s/4), g, |x|) has the exact sign of q - V
+// (v4 s/4 has few significant bits; the FMA rounds once). Every E2M1 rounding boundary is a multiple
+// of 1/4 and the next one is at least 1/2 away, so q lies within 1/8 and a few ulps of V, on the side
+// that d gives, and shares its code with V moved one ulp to that side (with V itself when d = 0, where
+// the conversion's ties-to-even is the rule's tie). The conversion (scale 1: nearest-even, saturating
+// at 6, sign kept) encodes that value. Groups whose s g is zero or outside [2^-124, 2^125] (so that
+// inv4 is finite and normal), or that hold a value that is not finite, take the exact tests.
+struct Nvfp4Snap {
+  float inv4;   // 4 rcp(s g)
+  float s4;     // s / 4, exact
+  bool exact;
+};
+
+__device__ __forceinline__ Nvfp4Snap nvfp4_snap(float s, float g, bool finite) {
+  const float sg = s * g;
+  return {4.0f * __builtin_amdgcn_rcpf(sg), 0.25f * s, !(finite && sg >= 0x1p-124f && sg <= 0x1p125f)};
+}
+
+template <int N>
+__device__ __forceinline__ uint32_t nvfp4_codes_snap(const float* x, float s, float g, Nvfp4Snap sn) {
+  static_assert(N % 2 == 0 && N <= 8, "whole bytes of one word");
+  float r[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float a = __builtin_fabsf(x[i]);
+    const float v4 = __builtin_rintf(a * sn.inv4);
+    const uint32_t d = __float_as_uint(__builtin_fmaf(-(v4 * sn.s4), g, a));
+    // + 1 for d > 0, - 1 for d < 0 (d is never -0: |x| - p rounds an exact zero to +0)
+    const uint32_t vb = __float_as_uint(0.25f * v4) + (uint32_t)((int32_t)d >> 31) + ((0u - d) >> 31);
+    r[i] = __uint_as_float(vb | (__float_as_uint(x[i]) & 0x80000000u));
+  }
+  uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, r[0], r[1], 1.0f, 0);
+  if constexpr (N >= 4) w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, r[2], r[3], 1.0f, 1);
+  if constexpr (N >= 6) w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, r[4], r[5], 1.0f, 2);
+  if constexpr (N >= 8) w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, r[6], r[7], 1.0f, 3);
+  if (sn.exact) w = nvfp4_codes_exact<N>(x, s, g);
+  return w;
+}
+
 // Maximum of v >= 0 over the four lanes l, l ^ 16, l ^ 32, l ^ 48 of a wave, in every one of them: a
 // swap of odd and even 16-lane rows, then of the two 32-lane halves, each followed by a max (on the
 // bit patterns, which order non-negative floats as their values).

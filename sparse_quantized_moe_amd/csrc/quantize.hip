@@ -54,12 +54,16 @@ __device__ __forceinline__ void load_group(const void* x, int64_t off, float v[3
 
 // Quantize 32 values with global g: writes 16 code bytes and returns the scale byte. fp32 inputs take
 // the hardware conversion with its exact fallback; bf16 inputs (few significant bits, so quotients
-// often sit right on a boundary) take the exact comparisons directly.
+// often sit right on a boundary) take the one-test snap encoding.
 template <bool F32>
 __device__ __forceinline__ uint32_t quantize_group(const float v[32], float g, u32x4& out) {
   float amax = 0.0f;
+  uint32_t mb = 0;   // largest magnitude bit pattern: >= 0x7F800000 iff some value is not finite
 #pragma unroll
-  for (int i = 0; i < 32; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
+  for (int i = 0; i < 32; ++i) {
+    amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
+    if (!F32) mb = __builtin_elementwise_max(mb, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+  }
   const int sc = scale_code(amax, g);
   const float s = e4m3_value(sc);
   if (F32) {
@@ -69,10 +73,11 @@ __device__ __forceinline__ uint32_t quantize_group(const float v[32], float g, u
     out.z = nvfp4_codes<8>(v + 16, s, g, rc);
     out.w = nvfp4_codes<8>(v + 24, s, g, rc);
   } else {
-    out.x = nvfp4_codes_exact<8>(v, s, g);
-    out.y = nvfp4_codes_exact<8>(v + 8, s, g);
-    out.z = nvfp4_codes_exact<8>(v + 16, s, g);
-    out.w = nvfp4_codes_exact<8>(v + 24, s, g);
+    const Nvfp4Snap sn = nvfp4_snap(s, g, mb < 0x7F800000u);
+    out.x = nvfp4_codes_snap<8>(v, s, g, sn);
+    out.y = nvfp4_codes_snap<8>(v + 8, s, g, sn);
+    out.z = nvfp4_codes_snap<8>(v + 16, s, g, sn);
+    out.w = nvfp4_codes_snap<8>(v + 24, s, g, sn);
   }
   return (uint32_t)sc;
 }

@@ -263,11 +263,14 @@ __device__ void route_tile(const RouteArgs& a, int tile, uint8_t* smem) {
   }
 }
 
+// Experts encoded per load of a token's values, at most.
+constexpr int kQuantRun = 8;
+
 // One item = (token t, run jc of its experts, 32-group grp); consecutive threads take consecutive
 // groups of one token. The per-expert globals sit in LDS and a run's ids are loaded with the token's
 // values, so an item costs one round trip to memory.
 template <int KMAX>
-__device__ void route_quantize(const RouteArgs& a, int qb, float* s_g) {
+__device__ __forceinline__ void route_quantize(const RouteArgs& a, int qb, float* s_g) {
   for (int e = threadIdx.x; e < a.E; e += kRouteThreads) s_g[e] = a.a_global[e];
   __syncthreads();
   const uint32_t G = (uint32_t)(a.H >> 5);
@@ -296,8 +299,13 @@ __device__ void route_quantize(const RouteArgs& a, int qb, float* s_g) {
       }
     }
     float amax = 0.0f;
+    uint32_t mb = 0;   // largest magnitude bit pattern: >= 0x7F800000 iff some value is not finite
 #pragma unroll
-    for (int i = 0; i < 32; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
+    for (int i = 0; i < 32; ++i) {
+      amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
+      mb = __builtin_elementwise_max(mb, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+    }
+    const bool finite = mb < 0x7F800000u;
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
       const int e = ids[j];
@@ -306,9 +314,10 @@ __device__ void route_quantize(const RouteArgs& a, int qb, float* s_g) {
       const float g = s_g[e];
       const int sc = scale_code(amax, g);
       const float s = e4m3_value(sc);
+      const Nvfp4Snap sn = nvfp4_snap(s, g, finite);
       uint32_t w[4];
 #pragma unroll
-      for (int h = 0; h < 4; ++h) w[h] = nvfp4_codes_exact<8>(v + 8 * h, s, g);
+      for (int h = 0; h < 4; ++h) w[h] = nvfp4_codes_snap<8>(v + 8 * h, s, g, sn);
       *reinterpret_cast<u32x4*>(a.codes + p * (a.H >> 1) + grp * 16) = u32x4{w[0], w[1], w[2], w[3]};
       a.scales[p * G + grp] = (uint8_t)sc;
     }
@@ -319,7 +328,7 @@ template <int KMAX>
 __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   if ((int)blockIdx.x < a.ntiles) route_tile<KMAX>(a, blockIdx.x, smem);
-  else route_quantize<KMAX>(a, blockIdx.x - a.ntiles, reinterpret_cast<float*>(smem));
+  else route_quantize<(KMAX < kQuantRun ? KMAX : kQuantRun)>(a, blockIdx.x - a.ntiles, reinterpret_cast<float*>(smem));
 }
 
 // Several tiles: per expert, the exclusive prefix of the tile counts becomes each (tile, expert)'s
@@ -397,8 +406,10 @@ void launch_route(const int* ids, int64_t T, int k, int E, int* counts, int* off
   if (x && T > 0) {
     // enough items to spread a small batch over the chip; a large one encodes all k experts per load
     const int64_t tg = T * (H >> 5);
+    // (runs of at most kQuantRun experts, the quantizer's register budget)
     int64_t nj = (131072 + tg - 1) / tg;
     nj = nj < 1 ? 1 : (nj > k ? k : nj);
+    if (nj < (k + kQuantRun - 1) / kQuantRun) nj = (k + kQuantRun - 1) / kQuantRun;
     a.kchunk = (int)((k + nj - 1) / nj);
     nj = (k + a.kchunk - 1) / a.kchunk;
     const int64_t qb = (tg * nj + kRouteThreads - 1) / kRouteThreads;
