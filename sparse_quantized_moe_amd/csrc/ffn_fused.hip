@@ -337,7 +337,7 @@ __global__ __launch_bounds__(kFzThreads) __attribute__((amdgpu_waves_per_eu(3)))
   lds_barrier();
   {
     // NVFP4 codes of every pair's activation row (this workgroup's share of the (pair, 32-group)
-    // items), exact comparisons: bf16 inputs
+    // items), the one-test snap encoding: bf16 inputs
     auto quantize_item = [&](int it, int p, int ex, const u32x4 (&xv)[4]) {
       if (ex < 0 || ex >= E) return;
       const int grp = it - p * G13;
@@ -352,14 +352,19 @@ __global__ __launch_bounds__(kFzThreads) __attribute__((amdgpu_waves_per_eu(3)))
         }
       }
       float amax = 0.0f;
+      uint32_t mb = 0;   // largest magnitude bit pattern: >= 0x7F800000 iff some value is not finite
 #pragma unroll
-      for (int i = 0; i < 32; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
+      for (int i = 0; i < 32; ++i) {
+        amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
+        mb = __builtin_elementwise_max(mb, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+      }
       const float g = s_g[ex];
       const int sc = scale_code(amax, g);
       const float s = e4m3_value(sc);
+      const Nvfp4Snap sn = nvfp4_snap(s, g, mb < 0x7F800000u);
       uint32_t w[4];
 #pragma unroll
-      for (int h = 0; h < 4; ++h) w[h] = nvfp4_codes_exact<8>(v + 8 * h, s, g);
+      for (int h = 0; h < 4; ++h) w[h] = nvfp4_codes_snap<8>(v + 8 * h, s, g, sn);
       epi_store<kCpolDevice>(reinterpret_cast<u32x4*>(a.a13c), (int64_t)p * (H >> 5) + grp, u32x4{w[0], w[1], w[2], w[3]});
       epi_store<kCpolDevice>(a.a13s, (int64_t)p * G13 + grp, (uint8_t)sc);
     };
