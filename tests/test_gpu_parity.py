@@ -87,6 +87,32 @@ def test_quantize_f32_boundaries_bit_exact(spread):
     assert np.array_equal(codes.cpu().numpy(), rc)
 
 
+def test_quantize_bf16_boundaries_bit_exact():
+    """bf16 inputs on every E2M1 rounding boundary and one bf16 ulp either side. With a power-of-two
+    global, B·s·g has at most 7 significant bits and is itself a bf16 value, so exact ties occur (the
+    case where the bf16 encoder relies on the conversion's nearest-even)."""
+    rng = np.random.default_rng(29)
+    R = 512
+    g = np.float32(2.0 ** -5)
+    x = np.zeros((R, 64), np.float32)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    for r in range(R):
+        s = float(nvfp4.E4M3_MAGNITUDES[rng.integers(8, 0x7E)])
+        for gi in range(2):
+            v = (rng.choice(mids, 32) * s * float(g)).astype(np.float32)
+            b = (v.view(np.uint32) >> 16).astype(np.int64) + rng.integers(-1, 2, 32)
+            v = (b.astype(np.uint32) << 16).view(np.float32)
+            v[0] = np.float32(6 * s * float(g))   # amax = 6 s g: the group's scale is s
+            v *= np.where(rng.random(32) < 0.5, -1, 1).astype(np.float32)
+            x[r, 32 * gi:32 * gi + 32] = v
+    xt = torch.from_numpy(x).to(torch.bfloat16)
+    assert np.array_equal(xt.float().numpy(), x)   # every input is a bf16 value
+    codes, scales = moesq.quantize_act(xt.to(DEV), torch.tensor([g], device=DEV))
+    rc, rs = nvfp4.quantize(x.astype(np.float64), np.float64(g))
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
 def test_quantize_gather_with_expert_globals():
     T, H, E = 40, 256, 5
     x = synth.activations(4, T, H, device=DEV)
