@@ -179,3 +179,24 @@ def check_admissible(x, x_err, g, codes, scales):
     sign = (c >> 3) & 1
     ok_sign = (sign == np.signbit(x.reshape(R, K // 32, 32))) | (ax <= er)
     return ok_s & (ok_m & ok_sign).all(axis=2)
+
+
+def ambiguous_groups(x, x_err, g):
+    """True per group when more than one encoding is admissible (``check_admissible``): the scale
+    interval holds two bytes, or at the nearest-even scale some code interval holds two codes, or some
+    |x_i| <= err_i (either sign). Groups that are not ambiguous have exactly one correct encoding."""
+    x = np.asarray(x, dtype=np.float64)
+    err = np.asarray(x_err, dtype=np.float64)
+    R, K = x.shape
+    g = np.broadcast_to(np.asarray(g, dtype=np.float64).reshape(-1, 1), (R, 1))
+    s_lo, s_hi = admissible(x, err, g)
+    _, s_mid = quantize(x, g)
+    sg = E4M3_MAGNITUDES[s_mid] * g
+    ax = np.abs(x).reshape(R, K // 32, 32)
+    er = err.reshape(R, K // 32, 32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r_lo = np.where(sg[..., None] > 0, np.maximum(ax - er, 0.0) / sg[..., None], 0.0)
+        r_hi = np.where(sg[..., None] > 0, (ax + er) / sg[..., None], 0.0)
+    code_amb = (e2m1_rne_sat(r_lo) != e2m1_rne_sat(r_hi)).any(axis=2)
+    sign_amb = (ax <= er).any(axis=2)
+    return (s_lo != s_hi) | code_amb | sign_amb

@@ -3,9 +3,16 @@
 Bit-exact: the permutation and the gate/up input codes/scales (exact inputs, exact decisions).
 The down input (quantized h) may differ from the oracle only where the oracle's own decision lies
 within the HIP path's fp32 error bound of a rounding boundary (both neighbours are correct results);
-every such group must be one of the oracle's admissible encodings. The final output is compared
-row by row (max |y - yref| / max |yref| <= 1e-3) with the oracle's output computed from the admissible
-encoding the GPU picked, so a legitimate tie flip does not fail the test and anything else does.
+every such group must be one of the oracle's admissible encodings, and the number of such flips is
+capped by the number of groups whose admissible set holds more than one encoding. Two output gates:
+
+* teacher-forced: the oracle's output recomputed from the admissible encoding the GPU picked, compared
+  row by row (max |y - yref| / max |yref| <= 1e-3 on every row);
+* non-forced: the oracle's own output, compared tensor-normwise (max |y - yref| / max |yref| <= 1e-3
+  over all compared rows), with the rows above 1e-3 row-normwise counted and each required to hold a
+  flipped group.
+
+Rows whose oracle output is exactly zero (every pair of the token dropped) must be exactly zero.
 """
 from __future__ import annotations
 
@@ -32,8 +39,11 @@ def oracle_layer(dense_expert, experts):
 
 
 def gamma_for(K: int) -> float:
-    # fp32 accumulation of 64-K sparse-MFMA partial sums: K/64 additions plus the MFMA's own 32-term sum
-    return K / 64.0 + 64.0
+    # The sparse MFMA adds its products to the fp32 accumulator in groups of 8 kept products (16 dense
+    # K), one rounding per group (measured on gfx950 with an accumulator of 1 and equal tiny products):
+    # K/16 roundings along K, each at most one unit of the running sum, plus a margin for the
+    # epilogue's global-scale products.
+    return K / 16.0 + 16.0
 
 
 def compare_ffn(x, ids, wts, ow13, ow2, g13, g2, gpu_out, gpu, tokens=None, E=None):
@@ -62,14 +72,20 @@ def compare_ffn(x, ids, wts, ow13, ow2, g13, g2, gpu_out, gpu, tokens=None, E=No
         nvfp4.unpack_codes(a2c_gpu).reshape(-1, I // 32, 32) ==
         nvfp4.unpack_codes(inter["a2_codes"]).reshape(-1, I // 32, 32)).all(axis=2)
     n_diff = int((~same).sum())
+    out_own = out_ref
     adopted_c = inter["a2_codes"].copy()
     adopted_s = inter["a2_scales"].copy()
+    n_amb = 0
     if n_diff:
         bound = moe.h_error_bound(xs, ids_s, ow13, g13, g2, gamma_for(H))
         ge = np.asarray(g2, np.float64)[ids_s.ravel()[p_sub]]
         ok = nvfp4.check_admissible(inter["h"], bound, ge, a2c_gpu, a2s_gpu)
         bad = (~same) & (~ok)
         assert not bad.any(), f"{int(bad.sum())} down-input groups are not an admissible encoding"
+        n_amb = int(nvfp4.ambiguous_groups(inter["h"], bound, ge).sum())
+        # an unbiased fp32 error far inside its worst-case bound flips a small share of the groups
+        # that lie within the bound of a boundary; a systematic shift of h would flip most of them
+        assert n_diff <= max(3, n_amb // 2), f"{n_diff} flipped groups of {n_amb} ambiguous ones"
         rows_d, grp_d = np.nonzero(~same)
         cu = nvfp4.unpack_codes(adopted_c)
         cg = nvfp4.unpack_codes(a2c_gpu)
@@ -79,9 +95,21 @@ def compare_ffn(x, ids, wts, ow13, ow2, g13, g2, gpu_out, gpu, tokens=None, E=No
         adopted_c = (cu[:, 0::2] | (cu[:, 1::2] << 4)).astype(np.uint8)
         out_ref = moe.down_combine(adopted_c, adopted_s, g2, inter["offsets"], p_sub, wts_s, ow2, len(tok), H)
     y = np.asarray(gpu_out, np.float64)[tok]
-    err = np.abs(y - out_ref).max(axis=1) / np.maximum(np.abs(out_ref).max(axis=1), 1e-300)
-    nz = np.abs(out_ref).max(axis=1) > 0
-    worst = float(err[nz].max()) if nz.any() else 0.0
+    den = np.abs(out_ref).max(axis=1)
+    zero = den == 0
+    assert (y[zero] == 0).all(), "rows with every pair dropped must be exactly zero"
+    err = np.abs(y - out_ref).max(axis=1) / np.maximum(den, 1e-300)
+    worst = float(err[~zero].max()) if (~zero).any() else 0.0
     assert worst <= TOL, f"row-normwise error {worst:.3e} > {TOL}"
-    return {"rows": int(len(tok)), "max_row_rel_err": worst, "admissible_flips": n_diff,
+    # non-forced: against the oracle's own encoding of h
+    dev = np.abs(y - out_own)
+    tensor_err = float(dev.max() / max(np.abs(out_own).max(), 1e-300))
+    assert tensor_err <= TOL, f"non-forced tensor-normwise error {tensor_err:.3e} > {TOL}"
+    row_own = dev.max(axis=1) / np.maximum(np.abs(out_own).max(axis=1), 1e-300)
+    hot = np.nonzero((row_own > TOL) & ~zero)[0]
+    if len(hot):
+        tok_flipped = set((p_sub[np.nonzero((~same).any(axis=1))[0]] // k).tolist())
+        assert set(hot.tolist()) <= tok_flipped, "a row above 1e-3 (non-forced) without a flipped h group"
+    return {"rows": int(len(tok)), "max_row_rel_err": worst, "nonforced_tensor_err": tensor_err,
+            "nonforced_rows_above_tol": int(len(hot)), "admissible_flips": n_diff, "ambiguous_groups": n_amb,
             "groups": int(same.size)}
