@@ -1,19 +1,21 @@
 #!/usr/bin/env python3
 """Throughput of the paired-4:8 sparse NVFP4 MoE FFN on one MI355X.
 
-Metric: weight-stream GB/s at decode (stored sparse bytes of the experts a batch touches, per second
-of the whole moesq_moe_ffn call) on the 128-expert, top-8, hidden-2048, moe_intermediate-768 layer at
-T=256 tokens, and effective dense TFLOP/s (6*P*H*I per second, P = T*k) of the same layer at
-prefill, T=8192 with Zipf(1.1)-skewed routing.
+Headline: effective dense TFLOP/s (6*P*H*I per second of the whole moesq_moe_ffn call, P = live
+(token, expert) pairs) of the largest single-GPU layer: 384 experts, top-8, hidden 7168,
+moe_intermediate 2048, T=16384 tokens with Zipf(1.0)-skewed routing and 0.1 % activation outliers (one
+GPU's full share of a Kimi-K2-shaped layer). Beside it: the weight-stream GB/s (stored sparse bytes of
+the touched experts per second of the call) of the decode layers (128 experts at T=256, 512 experts at
+T=64) and the effective dense TFLOP/s of the other prefill layers.
 
 One step = one moesq_moe_ffn call (permute, quantize, gate/up GEMM + SiLU*up + quantize, down GEMM,
-top-k combine) over one batch already resident in HBM. The layer's weights (207.6 MB) fit in the
-256 MB Infinity Cache, so decode steps rotate over several copies of the weights (a cold-cache
-stream, the reported value) and the warm single-copy figure is reported beside it.
+top-k combine) over one batch already resident in HBM. The 128-expert layer's weights (207.6 MB) fit
+in the 256 MB last-level cache, so its decode steps rotate over several weight copies.
 
-Output: one JSON line (rank 0). ``roofline`` is for the dominant kernel (at decode the one-launch
-FFN kernel, else the gate/up GEMM), timed with HIP events recorded by the library on its own stream;
-``cpu_baseline`` times the CPU oracle on a bounded sample of the same decode workload.
+Output: one JSON line. ``roofline`` is the headline layer's dominant kernel (the gate/up GEMM; kept-half
+multiply-adds against the dense f16 MFMA peak), timed with HIP events its own dispatch records;
+every sub-object carries the rooflines of its GEMMs the same way. ``cpu_baseline`` times the CPU
+oracle on a bounded token sample of the headline layer.
 """
 from __future__ import annotations
 
@@ -266,45 +268,6 @@ def fold_figures(moesq, torch, ev, reps=20):
     return res
 
 
-def other_workloads(moesq, torch, ev, seed, dev, names=("e512_decode", "e512_prefill", "kimi_k2_prefill")):
-    """The other layer shapes, each timed on its own batch like the headline ones (no weight-copy
-    rotation: their touched weights are far larger than the 256 MB last-level cache): decode rows give
-    the weight-stream GB/s on the stored bytes of the touched experts, prefill rows the effective dense
-    TFLOP/s; both with each stage's kernel time."""
-    import synth
-    res = {}
-    for name in names:
-        wl = synth.WORKLOADS[name]
-        w13, w2, dense = build_layer(wl, seed, dev)
-        x, ids, wts, g13, g2 = batch(wl, seed, dev, dense)
-        ws = torch.empty(moesq.lib().moesq_moe_ffn_workspace_size(wl.T, wl.H, wl.I, wl.k, wl.E, 0),
-                         dtype=torch.uint8, device=dev)
-        out = torch.empty((wl.T, wl.H), dtype=torch.float32, device=dev)
-        decode = wl.T * wl.k <= 48 * wl.E
-        steps = 20 if decode else 5
-        a = (moesq, torch, ev, x, torch.from_numpy(ids).to(dev), torch.from_numpy(wts).to(dev), [(w13, w2)],
-             torch.from_numpy(g13).to(dev), torch.from_numpy(g2).to(dev), out, ws, 2, steps)
-        wall, _, _ = run_steps(*a)
-        _, st, _ = run_steps(*a, staged=True)
-        t = wall / steps
-        ns = len(moesq.FFN_STAGES)
-        r = {"tokens": wl.T, "experts": wl.E, "top_k": wl.k, "hidden": wl.H, "moe_intermediate": wl.I,
-             "us_per_step": round(t * 1e6, 2),
-             "kernel_us": {n: round(float(v) * 1e3, 2) for n, v in zip(moesq.FFN_STAGES, st.mean(axis=0)[ns:])}}
-        if decode:
-            n, wb = touched_bytes(ids, wl.E, wl.H, wl.I)
-            r.update({"metric": "weight-stream GB/s", "value": round(wb / t / 1e9, 2), "experts_touched": n,
-                      "stored_bytes_streamed": wb})
-        else:
-            P = int((ids >= 0).sum())
-            r.update({"metric": "effective dense TFLOP/s", "value": round(6.0 * P * wl.H * wl.I / t / 1e12, 2)})
-        log(f"{name}: {r['value']} {r['metric']}, {r['us_per_step']} us/step")
-        res[name] = r
-        del w13, w2, ws, out, x
-        torch.cuda.empty_cache()
-    return res
-
-
 def side_passes(wl, P, route_ms, combine_ms):
     """The two HBM-bound passes around the GEMMs, from their kernels' own start/end events: routing
     (router ids in; x in, bf16; activation codes and scales out; sorted and inv out) and the top-k
@@ -315,28 +278,40 @@ def side_passes(wl, P, route_ms, combine_ms):
             "combine": {"us": round(combine_ms * 1e3, 2), "bytes": cb, "GBps": round(cb / (combine_ms * 1e-3) / 1e9, 1)}}
 
 
-def cpu_baseline(wl, seed, x, ids, wts, g13, g2, dense_expert, ntok):
-    """The oracle (unchanged) on a bounded sample of the decode batch: ntok tokens and their experts."""
+def cpu_baseline(wl, seed, x, ids, wts, g13, g2, dense_expert, max_experts, metric):
+    """The oracle (unchanged) on a bounded sample of the workload: tokens drawn at random (seeded) as
+    long as the experts they name stay within ``max_experts``; the oracle's compression of those
+    experts runs first, untimed. metric "tflops": effective dense TFLOP/s (6 P H I per second over the
+    sample's pairs); "gbps": stored bytes of the sample's experts per second."""
     import multiprocessing
     from concurrent.futures import ProcessPoolExecutor
     from oracle import compress, moe
     import threadpoolctl
 
     rng = np.random.default_rng(seed)
-    toks = np.sort(rng.choice(wl.T, ntok, replace=False))
-    experts = sorted(set(ids[toks].ravel().tolist()) - {-1})
-    dense = {e: [t.cpu().numpy() for t in dense_expert(e)] for e in experts}
+    toks, experts = [], set()
+    for t in rng.permutation(wl.T):
+        e_t = set(ids[t].tolist()) - {-1}
+        if toks and len(experts | e_t) > max_experts:
+            break
+        toks.append(int(t))
+        experts |= e_t
+    toks = np.sort(np.array(toks))
+    experts = sorted(experts)
     t0 = time.time()
-    jobs = [(e, i) for e in experts for i in range(3)]
+    comp = {}
     with ProcessPoolExecutor(max_workers=min(16, os.cpu_count() or 1),
                              mp_context=multiprocessing.get_context("spawn")) as ex:
-        res = list(ex.map(compress.compress, [dense[e][i] for e, i in jobs]))
+        for b0 in range(0, len(experts), 16):
+            jobs = [(e, i) for e in experts[b0:b0 + 16] for i in range(3)]
+            dense = {e: [t.cpu().numpy() for t in dense_expert(e)] for e in experts[b0:b0 + 16]}
+            for (e, i), r in zip(jobs, ex.map(compress.compress, [dense[e][i] for e, i in jobs])):
+                comp[(e, i)] = r
     log(f"cpu baseline: oracle compression of {len(experts)} experts (not timed) {time.time() - t0:.1f}s")
-    by = {(e, i): r for (e, i), r in zip(jobs, res)}
     w13 = [dict(), dict(), dict(), dict()]
     w2 = [dict(), dict(), dict(), dict()]
     for e in experts:
-        cg, cu, cd = by[(e, 0)], by[(e, 1)], by[(e, 2)]
+        cg, cu, cd = comp[(e, 0)], comp[(e, 1)], comp[(e, 2)]
         for i in range(3):
             w13[i][e] = np.concatenate([cg[i], cu[i]])
             w2[i][e] = cd[i]
@@ -348,27 +323,146 @@ def cpu_baseline(wl, seed, x, ids, wts, g13, g2, dense_expert, ntok):
     t0 = time.perf_counter()
     moe.moe_ffn(xs, ids[toks], wts[toks], w13, w2, g13, g2)
     dt = time.perf_counter() - t0
+    P = int((ids[toks] >= 0).sum())
     n, nbytes = touched_bytes(ids[toks], wl.E, wl.H, wl.I)
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{ntok} of {wl.T} tokens of {wl.name} ({n} experts, {nbytes / 1e6:.1f} MB stored), "
-                      f"{dt:.2f}s fp64 NumPy"}
+    if metric == "tflops":
+        value, unit = 6.0 * P * wl.H * wl.I / dt / 1e12, "effective dense TFLOP/s"
+    else:
+        value, unit = nbytes / dt / 1e9, "GB/s"
+    return {"value": round(value, 6), "unit": unit, "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(toks)} of {wl.T} tokens of {wl.name} ({P} pairs, {n} experts), {dt:.2f}s fp64 NumPy"}
+
+
+def prefill_figure(moesq, torch, ev, wl, seed, dev, warmup, steps, peaks, layer=None):
+    """One prefill layer: effective dense TFLOP/s of the whole call (6 P H I per second, P live
+    pairs), each stage's kernel time, and the rooflines of the two GEMM kernels (kept-half
+    multiply-adds, 2 P N K / 2 flops, against the dense f16 MFMA peak), from the kernels' own
+    start/end events."""
+    w13, w2, dense = layer if layer else build_layer(wl, seed, dev)
+    x, ids, wts, g13, g2 = batch(wl, seed, dev, dense)
+    ws = torch.empty(moesq.lib().moesq_moe_ffn_workspace_size(wl.T, wl.H, wl.I, wl.k, wl.E, 0), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty((wl.T, wl.H), dtype=torch.float32, device=dev)
+    a = (moesq, torch, ev, x, torch.from_numpy(ids).to(dev), torch.from_numpy(wts).to(dev), [(w13, w2)],
+         torch.from_numpy(g13).to(dev), torch.from_numpy(g2).to(dev), out, ws, warmup, steps)
+    wall, _, gpu_ms = run_steps(*a)
+    _, st, _ = run_steps(*a, staged=True)
+    ns = len(moesq.FFN_STAGES)
+    m = st.mean(axis=0)
+    P = int((ids >= 0).sum())
+    t = wall / steps
+    eff = 6.0 * P * wl.H * wl.I / t / 1e12
+    gu_ms, dn_ms = float(m[ns + 1]), float(m[ns + 2])
+    gu_flops = 2.0 * P * (2 * wl.I) * wl.H / 2
+    dn_flops = 2.0 * P * wl.H * wl.I / 2
+    src = ("gemm.hip", "gemm_common.h", "moesq_device.h")
+
+    def roof(kname, flops, ms, tname):
+        ach = flops / (ms * 1e-3) / 1e12
+        return {"bound": "mfma", "kernel": kname, "achieved": round(ach, 2), "peak": F16_DENSE_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / F16_DENSE_PEAK_TFLOPS, 4), "traffic": _traffic(tname, src),
+                "algorithmic_flops_per_launch": flops, "avg_launch_ms": round(ms, 4),
+                "measured_peak": peaks["smfmac_f16_kept_TFLOPs"],
+                "frac_of_measured": round(ach / peaks["smfmac_f16_kept_TFLOPs"], 4)}
+    res = {"workload": wl.name, "experts": wl.E, "top_k": wl.k, "hidden": wl.H, "moe_intermediate": wl.I,
+           "tokens": wl.T, "pairs": P, "value": round(eff, 2), "unit": "effective dense TFLOP/s",
+           "ms_per_step": round(t * 1e3, 4), "gpu_ms_per_step": round(gpu_ms, 4), "steps": steps,
+           "stage_ms": {n: round(float(v), 4) for n, v in zip(moesq.FFN_STAGES, m)},
+           "kernel_ms": {n: round(float(v), 4) for n, v in zip(moesq.FFN_STAGES, m[ns:])},
+           "side_passes": side_passes(wl, P, float(m[ns]), float(m[ns + 3])),
+           "roofline": roof("k_gemm_prefill<gate_up>", gu_flops, gu_ms, f"traffic_gemm_gate_up_{wl.name}.json"),
+           "roofline_down": roof("k_gemm_prefill<down>", dn_flops, dn_ms, f"traffic_gemm_down_{wl.name}.json")}
+    log(f"{wl.name}: {t * 1e3:.3f} ms/step, {eff:.1f} effective dense TFLOP/s; kernels (ms) "
+        + ", ".join(f"{n}={v:.3f}" for n, v in zip(moesq.FFN_STAGES, m[ns:]))
+        + f"; gate/up {res['roofline']['frac']:.3f}, down {res['roofline_down']['frac']:.3f} of the f16 peak")
+    return res, (x, ids, wts, g13, g2, dense)
+
+
+def decode_figure(moesq, torch, ev, wl, seed, dev, warmup, steps, copies, peaks):
+    """One decode layer: weight-stream GB/s of the whole call (stored bytes of the touched experts per
+    second), rotating ``copies`` weight copies so the stream does not come from the 256 MB last-level
+    cache (when the layer is smaller than that), with the roofline of the gate/up kernel (its
+    algorithmic bytes: touched W13 stored bytes + activation codes in + down-input codes out)."""
+    w13, w2, dense = build_layer(wl, seed, dev)
+    layers = [(w13, w2)]
+    for _ in range(copies - 1):
+        layers.append(tuple(moesq.SparseWeights(w.packed.clone(), None, None, w.global_scale.clone(), w.layout, w.shape)
+                            for w in (w13, w2)))
+    x, ids, wts, g13, g2 = batch(wl, seed, dev, dense)
+    ids_t, wts_t = torch.from_numpy(ids).to(dev), torch.from_numpy(wts).to(dev)
+    g13_t, g2_t = torch.from_numpy(g13).to(dev), torch.from_numpy(g2).to(dev)
+    ws = torch.empty(moesq.lib().moesq_moe_ffn_workspace_size(wl.T, wl.H, wl.I, wl.k, wl.E, 0), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty((wl.T, wl.H), dtype=torch.float32, device=dev)
+    a = (moesq, torch, ev, x, ids_t, wts_t, layers, g13_t, g2_t, out, ws, warmup, steps)
+    wall, _, gpu_ms = run_steps(*a, flags=DEFAULT_FLAGS)
+    _, stages, st_gpu = run_steps(*a, staged=True, flags=DEFAULT_FLAGS)
+    ns = len(moesq.FFN_STAGES)
+    m = stages.mean(axis=0)
+    n_touched, wbytes = touched_bytes(ids, wl.E, wl.H, wl.I)
+    t = wall / steps
+    value = wbytes / t / 1e9
+    P = int((ids >= 0).sum())
+    fused = bool(moesq.ffn_layout(wl.T, wl.H, wl.I, wl.k, wl.E, DEFAULT_FLAGS)["fused"])
+    alt = None
+    if fused or moesq.ffn_layout(wl.T, wl.H, wl.I, wl.k, wl.E, moesq.FLAG_FUSED)["fused"]:
+        alt_flags = moesq.FLAG_UNFUSED if fused else moesq.FLAG_FUSED
+        wall_a, _, _ = run_steps(*a, flags=alt_flags)
+        alt = {"path": "separate launches" if fused else "one fused launch",
+               "us_per_step": round(wall_a / steps * 1e6, 2), "GBps": round(wbytes / (wall_a / steps) / 1e9, 2)}
+    wall_w, _, _ = run_steps(moesq, torch, ev, x, ids_t, wts_t, layers[:1], g13_t, g2_t, out, ws, warmup, steps,
+                             flags=DEFAULT_FLAGS)
+    warm = wbytes / (wall_w / steps) / 1e9
+    kbytes = n_touched * (2 * wl.I * wl.H * 11 // 32 + 8) + P * (wl.H // 2 + wl.H // 32) + P * (wl.I // 2 + wl.I // 32)
+    k_ms = float(m[ns + 1])
+    achieved = kbytes / (k_ms * 1e-3) / 1e9
+    dbytes = n_touched * (wl.H * wl.I * 11 // 32 + 4) + P * (wl.I // 2 + wl.I // 32) + P * wl.H * 4
+    d_ms = float(m[ns + 2])
+    src = ("gemm.hip", "gemm_common.h", "moesq_device.h")
+    res = {"workload": wl.name, "experts": wl.E, "top_k": wl.k, "hidden": wl.H, "moe_intermediate": wl.I,
+           "tokens": wl.T, "value": round(value, 2), "unit": "weight-stream GB/s", "us_per_step": round(t * 1e6, 2),
+           "gpu_us_per_step": round(gpu_ms * 1e3, 2), "experts_touched": n_touched, "stored_bytes_streamed": wbytes,
+           "weight_copies_rotated": copies, "warm_cache_GBps": round(warm, 2), "fused_launch": fused,
+           "stage_us": {n: round(float(v) * 1e3, 2) for n, v in zip(moesq.FFN_STAGES, m)},
+           "kernel_us": {n: round(float(v) * 1e3, 2) for n, v in zip(moesq.FFN_STAGES, m[ns:])},
+           "other_path": alt,
+           "side_passes": side_passes(wl, P, float(m[ns]), float(m[ns + 3])),
+           "roofline": {"bound": "hbm", "kernel": "k_gemm_decode_stream<gate_up>", "achieved": round(achieved, 2),
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                        "traffic": _traffic(f"traffic_gemm_gate_up_{wl.name}.json", src),
+                        "algorithmic_bytes_per_launch": kbytes, "avg_launch_us": round(k_ms * 1e3, 2),
+                        "measured_peak": peaks["read_GBps"], "measured_peak_kind": "read stream (library probe)",
+                        "frac_of_measured": round(achieved / peaks["read_GBps"], 4)},
+           "roofline_down": {"bound": "hbm", "kernel": "k_gemm_decode_nloop<down>",
+                             "achieved": round(dbytes / (d_ms * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(dbytes / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                             "traffic": _traffic(f"traffic_gemm_down_{wl.name}.json", src),
+                             "algorithmic_bytes_per_launch": dbytes, "avg_launch_us": round(d_ms * 1e3, 2)}}
+    log(f"{wl.name}: {t * 1e6:.1f} us/step, {value:.1f} GB/s (warm {warm:.1f}); kernels (us) "
+        + ", ".join(f"{n}={v * 1e3:.1f}" for n, v in zip(moesq.FFN_STAGES, m[ns:]))
+        + f"; gate/up {res['roofline']['frac']:.3f} of 8 TB/s")
+    del layers
+    return res
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="qwen3_30b_decode")
-    ap.add_argument("--prefill-workload", default="qwen3_30b_prefill", help="'' to skip the prefill figure")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="kimi_k2_prefill",
+                    help="the headline layer (the largest single-GPU configuration)")
+    ap.add_argument("--decode-workloads", default="qwen3_30b_decode,e512_decode",
+                    help="decode layers reported beside the headline ('' for none)")
+    ap.add_argument("--prefill-workloads", default="qwen3_30b_prefill,e512_prefill",
+                    help="other prefill layers reported beside the headline ('' for none)")
     ap.add_argument("--copies", type=int, default=4, help="weight copies rotated at decode (cache-cold stream)")
-    ap.add_argument("--cpu-tokens", type=int, default=64,
-                    help="tokens of the decode batch the oracle baseline runs on (about 6-7 s of CPU work: nearly "
-                         "every expert is touched, and the per-expert dequantization dominates)")
+    ap.add_argument("--cpu-experts", type=int, default=32,
+                    help="experts the oracle baseline's token sample may name (about 15-20 s of fp64 NumPy at 384 "
+                         "experts, hidden 7168; the per-expert dequantization dominates)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the router, fold and measured-peak figures")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--no-other-workloads", action="store_true",
-                    help="skip the 512-expert and 384-expert layers (timed after the headline ones)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run 3 plain device copies of MIB MiB (a known-size kernel for scaling HBM "
                          "byte counters under rocprofv3 --pmc)")
@@ -395,144 +489,57 @@ def main():
         torch.cuda.synchronize()
         log(f"copy calibration: 3 copies of {n} bytes")
         del src, dst
-    peaks = measured_peaks(moesq, torch, ev)
-    log(f"measured: device copy {peaks['copy_GBps']} GB/s, read stream {peaks['read_GBps']} GB/s, smfmac f16 {peaks['smfmac_f16_kept_TFLOPs']} TFLOP/s (kept half)")
-    wl = synth.WORKLOADS[args.workload]
-    w13, w2, dense_expert = build_layer(wl, args.seed, dev)
-    layers = [(w13, w2)]
-    for _ in range(args.copies - 1):
-        layers.append(tuple(moesq.SparseWeights(w.packed.clone(), None, None, w.global_scale.clone(), w.layout, w.shape)
-                            for w in (w13, w2)))
-    x, ids, wts, g13, g2 = batch(wl, args.seed, dev, dense_expert)
-    ids_t, wts_t = torch.from_numpy(ids).to(dev), torch.from_numpy(wts).to(dev)
-    g13_t, g2_t = torch.from_numpy(g13).to(dev), torch.from_numpy(g2).to(dev)
-    ws = torch.empty(moesq.lib().moesq_moe_ffn_workspace_size(wl.T, wl.H, wl.I, wl.k, wl.E, 0), dtype=torch.uint8,
-                     device=dev)
-    out = torch.empty((wl.T, wl.H), dtype=torch.float32, device=dev)
-
-    wall, _, gpu_ms = run_steps(moesq, torch, ev, x, ids_t, wts_t, layers, g13_t, g2_t, out, ws,
-                                args.warmup, args.steps, flags=DEFAULT_FLAGS)
-    ms = wall / args.steps * 1e3
-    n_touched, wbytes = touched_bytes(ids, wl.E, wl.H, wl.I)
-    value = wbytes / (wall / args.steps) / 1e9
-    log(f"decode: {ms * 1e3:.1f} us/step wall, {gpu_ms * 1e3:.1f} us/step GPU events, {value:.1f} GB/s")
-    fused = bool(moesq.ffn_layout(wl.T, wl.H, wl.I, wl.k, wl.E, DEFAULT_FLAGS)["fused"])
-    # stage breakdown (events between the stages of every call), same rotation of weight copies; the
-    # one-launch path records all its stages around its single kernel
-    _, stages, st_gpu = run_steps(moesq, torch, ev, x, ids_t, wts_t, layers, g13_t, g2_t, out, ws,
-                                  args.warmup, args.steps, staged=True, flags=DEFAULT_FLAGS)
-    st_mean = stages.mean(axis=0)
-    log("decode stage us (mean): " + ", ".join(f"{n}={v * 1e3:.1f}" for n, v in zip(moesq.FFN_STAGES, st_mean))
-        + f"; {st_gpu * 1e3:.1f} us/step with stage events" + (" (one fused launch: all in the first)" if fused else "")
-        + "; kernels alone " + ", ".join(f"{n}={v * 1e3:.1f}" for n, v in zip(moesq.FFN_STAGES, st_mean[len(moesq.FFN_STAGES):])))
-    # the other path on the same batch, for comparison (separate launches vs the one-launch kernel)
-    alt = None
-    alt_flags = moesq.FLAG_UNFUSED if fused else moesq.FLAG_FUSED
-    if fused or moesq.ffn_layout(wl.T, wl.H, wl.I, wl.k, wl.E, moesq.FLAG_FUSED)["fused"]:
-        wall_a, _, _ = run_steps(moesq, torch, ev, x, ids_t, wts_t, layers, g13_t, g2_t, out, ws,
-                                 args.warmup, args.steps, flags=alt_flags)
-        _, st_a, _ = run_steps(moesq, torch, ev, x, ids_t, wts_t, layers, g13_t, g2_t, out, ws,
-                               args.warmup, args.steps, staged=True, flags=alt_flags)
-        alt = {"path": "separate launches" if fused else "one fused launch",
-               "us_per_step": round(wall_a / args.steps * 1e6, 2),
-               "GBps": round(wbytes / (wall_a / args.steps) / 1e9, 2),
-               "stage_us": {n: round(float(v) * 1e3, 2) for n, v in zip(moesq.FFN_STAGES, st_a.mean(axis=0))}}
-        log(f"decode, {alt['path']}: {alt['us_per_step']} us/step; stages {alt['stage_us']}")
-    # warm (single copy) figure
-    wall_w, _, _ = run_steps(moesq, torch, ev, x, ids_t, wts_t, layers[:1], g13_t, g2_t, out, ws,
-                             args.warmup, args.steps, flags=DEFAULT_FLAGS)
-    warm = wbytes / (wall_w / args.steps) / 1e9
-    P = int((ids >= 0).sum())
-    if fused:
-        # dominant (only) kernel: the fused FFN; algorithmic bytes = stored weight bytes of the touched
-        # experts + the tokens in (bf16) + router ids and weights + the output (fp32)
-        kname = "k_ffn_fused (route, gate/up, down, combine in one launch)"
-        kbytes = wbytes + wl.T * wl.H * 2 + P * 8 + wl.T * wl.H * 4
-        k_ms = float(st_mean[len(moesq.FFN_STAGES)])       # the one kernel, its own start/end events
-        tname, tsrc = "traffic_ffn_fused_qwen3_30b_decode.json", ("ffn_fused.hip", "gemm_common.h", "moesq_device.h")
+    if args.no_extras:
+        peaks = {"copy_GBps": None, "read_GBps": None, "smfmac_f16_kept_TFLOPs": None}
     else:
-        # dominant kernel: gate/up GEMM; algorithmic bytes = W13 stored bytes of touched experts + its
-        # activation input (codes + scales) + its output (down-input codes + scales)
-        kname = "k_gemm_decode_stream<gate_up>"
-        kbytes = n_touched * (2 * wl.I * wl.H * 11 // 32 + 8) + P * (wl.H // 2 + wl.H // 32) + P * (wl.I // 2 + wl.I // 32)
-        k_ms = float(st_mean[len(moesq.FFN_STAGES) + 1])   # the gate/up kernel, its own start/end events
-        tname, tsrc = "traffic_gemm_gate_up_qwen3_30b_decode.json", ("gemm.hip", "gemm_common.h", "moesq_device.h")
-    achieved = kbytes / (k_ms * 1e-3) / 1e9
-    traffic = _traffic(tname, tsrc)
+        peaks = measured_peaks(moesq, torch, ev)
+        log(f"measured: device copy {peaks['copy_GBps']} GB/s, read stream {peaks['read_GBps']} GB/s, "
+            f"smfmac f16 {peaks['smfmac_f16_kept_TFLOPs']} TFLOP/s (kept half)")
+    if peaks["smfmac_f16_kept_TFLOPs"] is None:
+        peaks = {"copy_GBps": 1.0, "read_GBps": 1.0, "smfmac_f16_kept_TFLOPs": 1.0}
+    wl = synth.WORKLOADS[args.workload]
+    decode_head = wl.T * wl.k <= 48 * wl.E
+    if decode_head:
+        head = decode_figure(moesq, torch, ev, wl, args.seed, dev, args.warmup, args.steps, args.copies, peaks)
+        layer = build_layer(wl, args.seed, dev) if not args.no_cpu_baseline else None
+        hx = batch(wl, args.seed, dev, layer[2]) if layer else None
+    else:
+        layer = build_layer(wl, args.seed, dev)
+        head, hx = prefill_figure(moesq, torch, ev, wl, args.seed, dev, args.warmup, args.steps, peaks, layer)
+        hx = hx[:5]
     result = {
         "metric": "MoE FFN effective dense TFLOP/s (prefill) + weight-stream GB/s (decode), 1 GPU",
-        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "value": head["value"], "unit": "GB/s" if decode_head else "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["us_per_step"] / 1e3 if decode_head else head["ms_per_step"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "nvfp4 w4a4 (f16 sparse MFMA, fp32 accumulate)", "data": "synthetic (seeded; random-init weights)",
-        "config": {"workload": wl.name, "experts": wl.E, "top_k": wl.k, "hidden": wl.H, "moe_intermediate": wl.I,
-                   "tokens": wl.T, "experts_touched": n_touched, "stored_bytes_streamed": wbytes,
-                   "weight_copies_rotated": args.copies, "warm_cache_GBps": round(warm, 2),
-                   "gpu_us_per_step": round(gpu_ms * 1e3, 2), "fused_launch": fused,
-                   "stage_us": {n: round(float(v) * 1e3, 2) for n, v in zip(moesq.FFN_STAGES, st_mean)},
-                   "kernel_us": {n: round(float(v) * 1e3, 2) for n, v in zip(moesq.FFN_STAGES, st_mean[len(moesq.FFN_STAGES):])},
-                   "other_path": alt},
-        "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 2),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "algorithmic_bytes_per_launch": kbytes,
-                     "avg_launch_us": round(k_ms * 1e3, 2),
-                     "measured_peak": peaks["read_GBps"], "measured_peak_kind": "read stream (library probe)",
-                     "frac_of_measured": round(achieved / peaks["read_GBps"], 4)},
-        "measured_peaks": peaks,
-        "side_passes": None if fused else side_passes(wl, P, float(st_mean[len(moesq.FFN_STAGES)]),
-                                                      float(st_mean[len(moesq.FFN_STAGES) + 3])),
-        "router": router_figures(moesq, torch, ev),
-        "fold_gate_up": fold_figures(moesq, torch, ev),
+        "config": {k: v for k, v in head.items() if k not in ("value", "unit", "roofline")},
+        "roofline": head["roofline"],
+        "measured_peaks": None if args.no_extras else peaks,
     }
-    del layers[1:]
-    torch.cuda.empty_cache()
-
-    if args.prefill_workload:
-        pw = synth.WORKLOADS[args.prefill_workload]
-        if (pw.E, pw.H, pw.I) != (wl.E, wl.H, wl.I):
-            w13, w2, dense_expert = build_layer(pw, args.seed, dev)
-        px, pids, pwts, pg13, pg2 = batch(pw, args.seed, dev, dense_expert)
-        pws = torch.empty(moesq.lib().moesq_moe_ffn_workspace_size(pw.T, pw.H, pw.I, pw.k, pw.E, 0),
-                          dtype=torch.uint8, device=dev)
-        pout = torch.empty((pw.T, pw.H), dtype=torch.float32, device=dev)
-        psteps = max(3, min(args.steps, 20))
-        pargs = (moesq, torch, ev, px, torch.from_numpy(pids).to(dev), torch.from_numpy(pwts).to(dev), [(w13, w2)],
-                 torch.from_numpy(pg13).to(dev), torch.from_numpy(pg2).to(dev), pout, pws, min(args.warmup, 3), psteps)
-        pwall, _, _ = run_steps(*pargs)
-        _, pst, _ = run_steps(*pargs, staged=True)
-        PP = int((pids >= 0).sum())
-        eff = 6.0 * PP * pw.H * pw.I / (pwall / psteps) / 1e12
-        pst_mean = pst.mean(axis=0)
-        g_ms = float(pst_mean[len(moesq.FFN_STAGES) + 1])  # the gate/up kernel, its own start/end events
-        alg_flops = 2.0 * PP * (2 * pw.I) * pw.H / 2          # multiply-adds on the kept half of W13
-        ach = alg_flops / (g_ms * 1e-3) / 1e12
-        log("prefill stage ms (mean): " + ", ".join(f"{n}={v:.3f}ms" for n, v in zip(moesq.FFN_STAGES, pst_mean))
-            + "; kernels alone " + ", ".join(f"{n}={v:.3f}ms" for n, v in zip(moesq.FFN_STAGES, pst_mean[len(moesq.FFN_STAGES):])))
-        log(f"prefill: {pwall / psteps * 1e3:.3f} ms/step, {eff:.1f} effective dense TFLOP/s")
-        result["prefill"] = {
-            "workload": pw.name, "tokens": pw.T, "value": round(eff, 2), "unit": "effective dense TFLOP/s",
-            "ms_per_step": round(pwall / psteps * 1e3, 4), "steps": psteps,
-            "stage_ms": {n: round(float(v), 4) for n, v in zip(moesq.FFN_STAGES, pst_mean)},
-            "kernel_ms": {n: round(float(v), 4) for n, v in zip(moesq.FFN_STAGES, pst_mean[len(moesq.FFN_STAGES):])},
-            "side_passes": side_passes(pw, PP, float(pst_mean[len(moesq.FFN_STAGES)]),
-                                       float(pst_mean[len(moesq.FFN_STAGES) + 3])),
-            "roofline": {"bound": "mfma", "kernel": "k_gemm_prefill<gate_up>",
-                         "achieved": round(ach, 2), "peak": F16_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(ach / F16_DENSE_PEAK_TFLOPS, 4),
-                         "traffic": _traffic(f"traffic_gemm_gate_up_{pw.name}.json", ("gemm.hip", "gemm_common.h", "moesq_device.h")),
-                         "algorithmic_flops_per_launch": alg_flops, "avg_launch_ms": round(g_ms, 4),
-                         "measured_peak": peaks["smfmac_f16_kept_TFLOPs"],
-                         "frac_of_measured": round(ach / peaks["smfmac_f16_kept_TFLOPs"], 4)},
-        }
-
-    if not args.no_other_workloads:
-        del layers, w13, w2
-        torch.cuda.empty_cache()
-        result["other_workloads"] = other_workloads(moesq, torch, ev, args.seed, dev)
-
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, args.seed, x, ids, wts, g13, g2, dense_expert, args.cpu_tokens)
+        w = layer[2]
+        x, ids, wts, g13, g2 = hx
+        result["cpu_baseline"] = cpu_baseline(wl, args.seed, x, ids, wts, g13, g2, w, args.cpu_experts,
+                                              "gbps" if decode_head else "tflops")
     else:
         result["cpu_baseline"] = None
+    del layer, hx
+    torch.cuda.empty_cache()
+    result["decode"] = {}
+    for name in [n for n in args.decode_workloads.split(",") if n]:
+        result["decode"][name] = decode_figure(moesq, torch, ev, synth.WORKLOADS[name], args.seed, dev, args.warmup,
+                                               max(args.steps, 20), args.copies, peaks)
+        torch.cuda.empty_cache()
+    result["prefill"] = {}
+    for name in [n for n in args.prefill_workloads.split(",") if n]:
+        result["prefill"][name] = prefill_figure(moesq, torch, ev, synth.WORKLOADS[name], args.seed, dev, args.warmup,
+                                                 args.steps, peaks)[0]
+        torch.cuda.empty_cache()
+    if not args.no_extras:
+        result["router"] = router_figures(moesq, torch, ev)
+        result["fold_gate_up"] = fold_figures(moesq, torch, ev)
     print(json.dumps(result), flush=True)
 
 

@@ -12,7 +12,8 @@
  * moesq_moe_ffn call the events its kernels record), so they are reentrant.
  *
  * Errors: a synchronous argument check returns a negative moesq_status and enqueues nothing; a launch
- * failure returns MOESQ_ERR_HIP with the HIP error text in moesq_last_error().
+ * failure (a kernel attribute that could not be set included) returns MOESQ_ERR_HIP with the HIP error
+ * text in moesq_last_error().
  *
  * Storage format (model card "Qwen3.5-397B-A17B-P48NVFP4-MoESQ", section "Sparse storage layout",
  * table of stored tensors): per expert linear [out = N, in = K]
@@ -37,7 +38,7 @@
 extern "C" {
 #endif
 
-#define MOESQ_ABI_VERSION 5
+#define MOESQ_ABI_VERSION 6
 /* quantization_config marker "paired48_sparse": {"layout": "pair-bitmask", "version": 1} */
 #define MOESQ_PAIR_BITMASK_VERSION 1
 
@@ -46,7 +47,9 @@ typedef enum {
   MOESQ_ERR_INVALID = -1,      /* a null pointer, a negative or inconsistent size, a bad enum */
   MOESQ_ERR_UNSUPPORTED = -2,  /* valid but outside what the kernels handle (a K not multiple of 256 ...) */
   MOESQ_ERR_WORKSPACE = -3,    /* workspace smaller than the size query returns */
-  MOESQ_ERR_HIP = -4           /* a HIP launch or synchronization failed; see moesq_last_error() */
+  MOESQ_ERR_HIP = -4,          /* a HIP launch or synchronization failed; see moesq_last_error() */
+  MOESQ_ERR_DEVICE = -5        /* (MOESQ_FLAG_SYNC_CHECK) a bounded device-side wait ran out: the
+                                  outputs of the call are not valid; see moesq_last_error() */
 } moesq_status;
 
 typedef enum { MOESQ_BF16 = 0, MOESQ_F32 = 1 } moesq_dtype;
@@ -152,8 +155,11 @@ moesq_status moesq_grouped_gemm(const uint8_t *a_codes, const uint8_t *a_scales,
  *   grid barriers (MOESQ_FLAG_FUSED; layout.fused = 1): same results and intermediates, except that
  *   tile_offsets and route_scratch are not written; `sync` is its barrier area (any initial
  *   contents). It assumes the device is not busy with other work holding CUs; if a barrier wait
- *   runs out (it should not), status[0] reads -1 and the outputs are not valid. Two fused calls on
- *   one workspace must not overlap in time. */
+ *   runs out (it should not), the outputs are not valid, status[0] may read -1, and a call with
+ *   MOESQ_FLAG_SYNC_CHECK returns MOESQ_ERR_DEVICE (it reads the launch's own failure word, tagged
+ *   with the launch, back from `sync` after the synchronization). Two fused calls on one workspace must not overlap in time.
+ *   Limits: T*k*max(H, I)/2 < 2^31 (32-bit buffer offsets of the activation codes), else
+ *   MOESQ_ERR_UNSUPPORTED. */
 typedef struct {
   size_t counts, offsets, tile_offsets, sorted, inv, status;
   size_t a13_codes, a13_scales, a2_codes, a2_scales, down_rows, route_scratch, sync;
@@ -195,6 +201,14 @@ moesq_status moesq_route_topk(const void *logits, moesq_dtype dtype, int64_t T, 
  * kernel, events[5..6] bracket it and events[7..12] are recorded right after it. NULL disables it.
  * The library keeps the pointer (thread-local) until it is reset; the caller keeps the array alive. */
 moesq_status moesq_set_stage_events(hipEvent_t *events /* host */, int32_t n);
+
+/* Failure-handling test hook: the number of polls after which a barrier wait of the one-launch decode
+ * path (MOESQ_FLAG_FUSED) gives up, for later moesq_moe_ffn calls on this host thread (thread-local;
+ * values above 2^32 - 1 are clamped). A negative value restores the default (2^20 polls, far beyond
+ * any healthy wait). The bound is checked before each poll, so 0 makes every wait give up at once
+ * while every workgroup still exits normally: the error path can be exercised without a stuck
+ * device (the call then returns MOESQ_ERR_DEVICE with MOESQ_FLAG_SYNC_CHECK). */
+moesq_status moesq_set_fused_spin_limit(int64_t polls);
 
 /* Measurement aid: a throughput probe of v_smfmac_f32_16x16x64_f16, the instruction the grouped GEMMs
  * are built on, so rooflines can be quoted against the rate this GPU sustains besides the published

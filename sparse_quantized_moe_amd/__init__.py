@@ -26,7 +26,7 @@ __all__ = [
 _PKG = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_PKG, "libmoesq.so")
 #: The C ABI version (MOESQ_ABI_VERSION in include/moesq.h) these bindings are declared for.
-ABI_VERSION = 5
+ABI_VERSION = 6
 FLAG_SYNC_CHECK = 1
 FLAG_UNFUSED = 2      # moe_ffn: separate launches even where the one-launch decode path applies
 FLAG_FUSED = 4        # moe_ffn: the one-launch decode path wherever it applies
@@ -38,12 +38,14 @@ EXPORTED_SYMBOLS = (
     "moesq_moe_ffn_workspace_size", "moesq_moe_ffn", "moesq_compress_weights", "moesq_validate_weights",
     "moesq_unpack_pair_bitmask", "moesq_pack_pair_bitmask", "moesq_set_stage_events", "moesq_tiled_bytes",
     "moesq_prepare_weights", "moesq_unprepare_weights", "moesq_permute_workspace_size", "moesq_probe_smfmac", "moesq_probe_read",
-    "moesq_route_topk", "moesq_fold_gate_up_globals",
+    "moesq_route_topk", "moesq_fold_gate_up_globals", "moesq_set_fused_spin_limit",
 )
 
 
 class MoesqError(RuntimeError):
-    pass
+    def __init__(self, msg: str, status: int = 0):
+        super().__init__(msg)
+        self.status = status
 
 
 class _CWeights(ctypes.Structure):
@@ -86,6 +88,7 @@ def _declare(L: ctypes.CDLL) -> None:
         "moesq_unpack_pair_bitmask": (ctypes.c_int, [_P, _P, _I64, _I32, _P, _P, _P]),
         "moesq_pack_pair_bitmask": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _P, _P]),
         "moesq_set_stage_events": (ctypes.c_int, [_P, _I32]),
+        "moesq_set_fused_spin_limit": (ctypes.c_int, [_I64]),
         "moesq_probe_smfmac": (ctypes.c_int, [_I32, _I32, _P, ctypes.POINTER(_I64), _P]),
         "moesq_probe_read": (ctypes.c_int, [_P, _I64, _P, _P]),
         "moesq_route_topk": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I32, _I32, _I32, _P, _P, _P]),
@@ -122,7 +125,7 @@ def abi_version() -> int:
 def _check(status: int) -> None:
     if status != 0:
         L = lib()
-        raise MoesqError(f"{L.moesq_status_string(status).decode()}: {L.moesq_last_error().decode()}")
+        raise MoesqError(f"{L.moesq_status_string(status).decode()}: {L.moesq_last_error().decode()}", status)
 
 
 def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
@@ -379,7 +382,14 @@ def set_stage_events(events) -> None:
         _check(lib().moesq_set_stage_events(ctypes.cast(events, ctypes.c_void_p), len(events)))
 
 
-__all__ += ["FFN_STAGES", "set_stage_events", "probe_smfmac", "probe_read", "route_topk"]
+def set_fused_spin_limit(polls: int) -> None:
+    """Polls after which a barrier wait of the one-launch decode path gives up, for later moe_ffn calls
+    on this thread (negative: the default; 0: every wait gives up at once); a failure-handling test
+    hook (see moesq_set_fused_spin_limit)."""
+    _check(lib().moesq_set_fused_spin_limit(polls))
+
+
+__all__ += ["FFN_STAGES", "set_stage_events", "set_fused_spin_limit", "probe_smfmac", "probe_read", "route_topk"]
 
 
 def route_topk(logits: torch.Tensor, k: int, renormalize: bool = True, out_ids: Optional[torch.Tensor] = None,

@@ -5,9 +5,28 @@
 #include "moesq.h"
 #include "moesq_internal.h"
 
+namespace moesq {
+
+namespace {
+thread_local hipError_t g_pending_hip_error = hipSuccess;
+}
+
+void note_hip_error(hipError_t e) {
+  if (g_pending_hip_error == hipSuccess) g_pending_hip_error = e;
+}
+
+hipError_t take_hip_error() {
+  const hipError_t e = g_pending_hip_error;
+  g_pending_hip_error = hipSuccess;
+  return e;
+}
+
+}  // namespace moesq
+
 namespace {
 
 thread_local std::string g_last_error;
+thread_local int64_t g_fused_spin_limit = -1;
 thread_local hipEvent_t* g_stage_events = nullptr;
 thread_local int g_stage_n = 0;
 
@@ -35,7 +54,9 @@ moesq_status fail(moesq_status s, const char* fmt, const char* what) {
   do { if (!(cond)) return fail(status, "%s", msg); } while (0)
 
 moesq_status check_launch(hipStream_t stream, bool sync) {
+  const hipError_t pending = moesq::take_hip_error();   // a launch skipped for a refused attribute
   hipError_t e = hipGetLastError();
+  if (pending != hipSuccess) e = pending;
   if (e == hipSuccess && sync) e = hipStreamSynchronize(stream);
   if (e != hipSuccess) return fail(MOESQ_ERR_HIP, "HIP error: %s", hipGetErrorString(e));
   return MOESQ_OK;
@@ -91,6 +112,7 @@ const char* moesq_status_string(moesq_status s) {
     case MOESQ_ERR_UNSUPPORTED: return "unsupported shape";
     case MOESQ_ERR_WORKSPACE: return "workspace too small";
     case MOESQ_ERR_HIP: return "HIP error";
+    case MOESQ_ERR_DEVICE: return "device-side wait ran out";
   }
   return "unknown status";
 }
@@ -101,6 +123,11 @@ moesq_status moesq_set_stage_events(hipEvent_t* events, int32_t n) {
   MOESQ_REQUIRE(!events || n >= 5, MOESQ_ERR_INVALID, "set_stage_events: need at least 5 events");
   g_stage_events = events;
   g_stage_n = events ? n : 0;
+  return MOESQ_OK;
+}
+
+moesq_status moesq_set_fused_spin_limit(int64_t polls) {
+  g_fused_spin_limit = polls < 0 ? -1 : (polls > 0xFFFFFFFFll ? 0xFFFFFFFFll : polls);
   return MOESQ_OK;
 }
 
@@ -246,8 +273,8 @@ moesq_status moesq_moe_ffn(const void* x, int64_t T, int32_t H, const int32_t* t
                 "moe_ffn: shapes must be w13 [2I, H], w2 [H, I]");
   MOESQ_REQUIRE(I % 256 == 0 && H % 256 == 0, MOESQ_ERR_UNSUPPORTED, "moe_ffn: H and I must be multiples of 256");
   MOESQ_REQUIRE(T * k < ((int64_t)1 << 31), MOESQ_ERR_UNSUPPORTED, "moe_ffn: T*k must fit in int32");
-  MOESQ_REQUIRE(T * k * (H / 2) < ((int64_t)1 << 31), MOESQ_ERR_UNSUPPORTED,
-                "moe_ffn: gate/up input codes must stay below 2 GiB (32-bit buffer offsets)");
+  MOESQ_REQUIRE(T * k * ((H > I ? H : I) / 2) < ((int64_t)1 << 31), MOESQ_ERR_UNSUPPORTED,
+                "moe_ffn: the gate/up and down input codes must stay below 2 GiB (32-bit buffer offsets)");
   if (T == 0) return MOESQ_OK;
   MOESQ_REQUIRE(x && topk_ids && topk_weights && a13_global && a2_global && out && workspace, MOESQ_ERR_INVALID,
                 "moe_ffn: null pointer");
@@ -279,17 +306,30 @@ moesq_status moesq_moe_ffn(const void* x, int64_t T, int32_t H, const int32_t* t
     f.T = T; f.H = H; f.I = I; f.k = k; f.E = E;
     f.counts = counts; f.offsets = offsets; f.sorted = sorted; f.inv = inv; f.status = status;
     f.a13c = a13c; f.a13s = a13s; f.a2c = a2c; f.a2s = a2s; f.D = drows; f.out = out; f.sync = ws + L.sync;
+    f.spin_limit = g_fused_spin_limit;
     stage_event(0, stream);
     hipError_t err;
+    unsigned ticket = 0;
     {
       const TimedKernel timed(0);
-      err = moesq::launch_ffn_fused(f, stream);
+      err = moesq::launch_ffn_fused(f, stream, &ticket);
     }
     for (int i = 1; i <= 4; ++i) stage_event(i, stream);
     if (g_stage_events && g_stage_n >= 13)
       for (int i = 7; i <= 12; ++i) stage_event(i, stream);   // the other stages: empty, after the kernel
     if (err != hipSuccess) return fail(MOESQ_ERR_HIP, "moe_ffn: fused launch: %s", hipGetErrorString(err));
-    return check_launch(stream, (flags & MOESQ_FLAG_SYNC_CHECK) != 0);
+    const bool sync = (flags & MOESQ_FLAG_SYNC_CHECK) != 0;
+    const moesq_status st = check_launch(stream, sync);
+    if (st != MOESQ_OK || !sync) return st;
+    // the kernel tags its error word with the launch's ticket when a barrier wait ran out
+    unsigned word = 0;
+    hipError_t e = hipMemcpyAsync(&word, ws + L.sync + moesq::kFusedErrOffset, sizeof word, hipMemcpyDeviceToHost,
+                                  stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return fail(MOESQ_ERR_HIP, "moe_ffn: reading the barrier error word: %s", hipGetErrorString(e));
+    if (word == ticket)
+      return fail(MOESQ_ERR_DEVICE, "%s", "moe_ffn: a barrier wait of the one-launch path ran out; outputs are not valid");
+    return MOESQ_OK;
   }
 
   // routing: permutation + gate/up input quantization (pair order)

@@ -71,6 +71,7 @@ struct FusedArgs {
   unsigned* err;                // error word (ticket of the failed launch)
   unsigned long long* flags;    // [grid] arrival flags
   unsigned ticket;              // unique per launch, non-zero
+  uint32_t spin_limit;          // polls before a barrier wait gives up
 };
 
 __host__ __device__ constexpr size_t fused_lds_bytes(int H, int I, int P) {
@@ -104,18 +105,19 @@ __device__ bool fz_grid_wait(const FusedArgs& a, unsigned round) {
   const unsigned long long tag = (unsigned long long)a.ticket << 32;
   const unsigned long long want = tag | round;
   auto failed = [&](uint32_t spins) {
-    return spins >= kFzSpinLimit || __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.ticket;
+    return spins >= a.spin_limit || __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.ticket;
   };
   auto reached = [&](unsigned long long v) { return (v & 0xFFFFFFFF00000000ull) == tag && v >= want; };
   bool ok = true;
   if (lane == 0) __hip_atomic_store(a.flags + blockIdx.x, want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // the bound is checked before each poll, so a limit of 0 gives up at once (the host's test hook)
   if (blockIdx.x == 0) {                              // the collector: every flag at this round
     for (uint32_t spins = 0;; ++spins) {
+      if (__shfl(failed(spins) ? 1 : 0, 0)) { ok = false; break; }
       bool mine = true;
       for (unsigned b = lane; b < gridDim.x; b += 64)
         mine = mine && reached(__hip_atomic_load(a.flags + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
       if (__all(mine)) break;
-      if (failed(spins)) { ok = false; break; }
       __builtin_amdgcn_s_sleep(1);
     }
     if (lane == 0 && ok) __hip_atomic_store(a.release, want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -123,8 +125,8 @@ __device__ bool fz_grid_wait(const FusedArgs& a, unsigned round) {
   if (lane == 0) {
     if (ok) {
       for (uint32_t spins = 0;; ++spins) {
-        if (reached(__hip_atomic_load(a.release, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) break;
         if (failed(spins)) { ok = false; break; }
+        if (reached(__hip_atomic_load(a.release, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) break;
         __builtin_amdgcn_s_sleep(1);
       }
     }
@@ -150,14 +152,16 @@ __device__ bool fz_expert_wait(const FusedArgs& a, unsigned round, int e) {
   if (lane == 0) __hip_atomic_store(a.flags + blockIdx.x, want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   bool ok = true;
   for (uint32_t spins = 0;; ++spins) {
+    const bool give_up =
+        spins >= a.spin_limit || __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.ticket;
+    if (__shfl(give_up ? 1 : 0, 0)) {
+      ok = false;
+      break;
+    }
     bool mine = true;
     for (int b = lane; b < a.parts; b += 64)
       mine = mine && reached(__hip_atomic_load(a.flags + e * a.parts + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
     if (__all(mine)) break;
-    if (spins >= kFzSpinLimit || __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.ticket) {
-      ok = false;
-      break;
-    }
     __builtin_amdgcn_s_sleep(1);
   }
   if (lane == 0 && !ok) {
@@ -609,9 +613,10 @@ bool fused_applicable(int64_t T, int H, int I, int k, int E) {
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
   static std::atomic<size_t> granted{0};   // always the same (largest) size, so racing first calls agree
   if (lds > granted.load(std::memory_order_relaxed)) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_ffn_fused), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)fused_lds_bytes(kFzMaxK, kFzMaxK, kFzMaxPairs)) != hipSuccess)
-      return false;
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_ffn_fused),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)fused_lds_bytes(kFzMaxK, kFzMaxK, kFzMaxPairs));
+    if (e != hipSuccess) return false;          // the separate launches serve the call instead
     granted.store(fused_lds_bytes(kFzMaxK, kFzMaxK, kFzMaxPairs), std::memory_order_relaxed);
   }
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&k_ffn_fused), kFzThreads,
@@ -621,7 +626,7 @@ bool fused_applicable(int64_t T, int H, int I, int k, int E) {
   return grid <= (int64_t)per_cu * cus && grid <= kFzMaxGrid;
 }
 
-hipError_t launch_ffn_fused(const FusedLaunch& f, hipStream_t stream) {
+hipError_t launch_ffn_fused(const FusedLaunch& f, hipStream_t stream, unsigned* ticket_out) {
   // launch tickets: odd (so never zero), distinct per launch of this process, seeded by the process id
   static std::atomic<unsigned> next_ticket{(unsigned)(0x9E3779B9u * (unsigned)getpid()) | 1u};
   const unsigned ticket = next_ticket.fetch_add(2u, std::memory_order_relaxed);
@@ -632,9 +637,11 @@ hipError_t launch_ffn_fused(const FusedLaunch& f, hipStream_t stream) {
   a.counts = f.counts; a.offsets = f.offsets; a.sorted = f.sorted; a.inv = f.inv; a.status = f.status;
   a.a13c = f.a13c; a.a13s = f.a13s; a.a2c = f.a2c; a.a2s = f.a2s; a.D = f.D; a.out = f.out;
   a.release = reinterpret_cast<unsigned long long*>(f.sync);
-  a.err = reinterpret_cast<unsigned*>(f.sync + 8);
+  a.err = reinterpret_cast<unsigned*>(f.sync + kFusedErrOffset);
   a.flags = reinterpret_cast<unsigned long long*>(f.sync + 64);
   a.ticket = ticket;
+  a.spin_limit = f.spin_limit >= 0 ? (uint32_t)f.spin_limit : kFzSpinLimit;
+  *ticket_out = ticket;
   // A plain launch: the workgroups are all resident at once because each needs most of a CU's LDS
   // (at most one per CU) and the grid is no larger than the CU count times the occupancy the
   // runtime reports (fused_applicable). A cooperative launch, which would also check this, cost

@@ -702,13 +702,21 @@ size_t gemm_lds_bytes(int tactic, int K) {
 }
 
 // Every caller passes the same size for a given kernel, so concurrent first calls set the same value.
+// Returns false (and notes the error for the entry point to report) if the attribute is refused; the
+// caller then skips the launch.
 template <class Kern>
-static void set_lds_attr(Kern* k, size_t lds) {
+static bool set_lds_attr(Kern* k, size_t lds) {
   static std::atomic<size_t> done{0};   // largest size already granted for this kernel
   if (lds > done.load(std::memory_order_relaxed)) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const hipError_t e =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) {
+      note_hip_error(e);
+      return false;
+    }
     done.store(lds, std::memory_order_relaxed);
   }
+  return true;
 }
 
 // Workgroups per expert of the one-chunk decode kernel, and the fewest n-blocks one covers: enough
@@ -720,7 +728,7 @@ constexpr int kNloopMinBlocks = 4;
 template <int EPI, int LAYOUT, int RT, int DEPTH>
 static void launch_nloop(const GemmParams& p, dim3 grid, int nblocks, hipStream_t stream) {
   const size_t lds = DecGeom<DEPTH>::lds;
-  set_lds_attr(&k_gemm_decode_nloop<EPI, LAYOUT, RT, DEPTH>, lds);
+  if (!set_lds_attr(&k_gemm_decode_nloop<EPI, LAYOUT, RT, DEPTH>, lds)) return;
   launch_kernel(k_gemm_decode_nloop<EPI, LAYOUT, RT, DEPTH>, grid, dim3(kGemmThreads), lds, stream, p, nblocks);
 }
 
@@ -733,7 +741,7 @@ static void launch_decode(const GemmParams& p, hipStream_t stream) {
   if constexpr (EPI == kEpiGateUp && LAYOUT == 1) {
     if (p.K <= kStreamMaxK) {
       const size_t lds = stream_lds_bytes(p.K);
-      set_lds_attr(&k_gemm_decode_stream<EPI, RT, DEPTH>, stream_lds_bytes(kStreamMaxK));
+      if (!set_lds_attr(&k_gemm_decode_stream<EPI, RT, DEPTH>, stream_lds_bytes(kStreamMaxK))) return;
       const int waves = (p.N >> 1) / 32;
       const int groups = (waves + kStreamWaves - 1) / kStreamWaves;
       launch_kernel(k_gemm_decode_stream<EPI, RT, DEPTH>, dim3((unsigned)p.E, (unsigned)groups), dim3(kStreamThreads), lds,
@@ -757,7 +765,7 @@ static void launch_decode(const GemmParams& p, hipStream_t stream) {
     }
   }
   const size_t lds = DecGeom<DEPTH>::lds;
-  set_lds_attr(&k_gemm_decode<EPI, LAYOUT, RT>, lds);
+  if (!set_lds_attr(&k_gemm_decode<EPI, LAYOUT, RT>, lds)) return;
   launch_kernel(k_gemm_decode<EPI, LAYOUT, RT>, dim3((unsigned)p.E, (unsigned)nblocks), dim3(kGemmThreads), lds, stream, p);
 }
 
@@ -765,7 +773,7 @@ template <int EPI, int LAYOUT>
 static void launch_prefill(const GemmParams& p, hipStream_t stream) {
   const size_t lds = gemm_lds_bytes(kTacticPrefill, p.K);
   constexpr int NWP = prefill_waves<EPI, LAYOUT>();
-  set_lds_attr(&k_gemm_prefill<EPI, LAYOUT, NWP>, lds);
+  if (!set_lds_attr(&k_gemm_prefill<EPI, LAYOUT, NWP>, lds)) return;
   // an upper bound of the live m-blocks (each expert adds at most one partial m-block); the kernel
   // spreads the live items over the XCDs and the rest of the grid exits
   const int64_t mblocks = (p.rows + kPreBMT - 1) / kPreBMT + p.E;

@@ -103,10 +103,14 @@ struct FusedLaunch {
   float* D;
   float* out;
   uint8_t* sync;      // kFusedSyncBytes of workspace: release word, error word, arrival flags (any contents)
+  int64_t spin_limit;   // polls before a barrier wait gives up (negative: the default)
 };
 constexpr size_t kFusedSyncBytes = 64 + 8 * 1024;
 bool fused_applicable(int64_t T, int H, int I, int k, int E);
-hipError_t launch_ffn_fused(const FusedLaunch& f, hipStream_t stream);
+// Enqueues the one-launch path; *ticket receives the launch's ticket, which the kernel writes into
+// the error word (sync + kFusedErrOffset) if one of its barrier waits runs out.
+hipError_t launch_ffn_fused(const FusedLaunch& f, hipStream_t stream, unsigned* ticket);
+constexpr size_t kFusedErrOffset = 8;
 
 // Router softmax top-k (router.hip): E <= 1024, 1 <= k <= min(E, 64).
 void launch_route_topk(const void* logits, bool f32, int64_t T, int E, int k, bool renormalize, int* ids,
@@ -115,6 +119,11 @@ void launch_route_topk(const void* logits, bool f32, int64_t T, int E, int k, bo
 // smfmac throughput probe (probe.hip): returns the number of instructions the launch issues.
 int64_t launch_probe_smfmac(int blocks, int iters, float* sink, hipStream_t stream);
 void launch_probe_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
+
+// A host-side HIP failure met while preparing a launch (a kernel attribute that could not be set):
+// the launch is skipped and the error is reported by the calling entry point (thread-local).
+void note_hip_error(hipError_t e);
+hipError_t take_hip_error();
 
 // out[t][:] = sum_j D[inv[t*k + j]][:] (rows with inv < 0 skipped), in j order.
 void launch_combine(const float* D, const int* inv, int64_t T, int k, int H, float* out, hipStream_t stream);

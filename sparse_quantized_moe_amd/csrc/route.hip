@@ -392,11 +392,18 @@ void launch_route(const int* ids, int64_t T, int k, int E, int* counts, int* off
                   int* sorted, int* inv, int* status, void* scratch, const uint16_t* x, int H, const float* a_global,
                   uint8_t* codes, uint8_t* scales, hipStream_t stream) {
   static std::once_flag attr;
+  static hipError_t attr_err = hipSuccess;   // written once, inside call_once, read after it
   std::call_once(attr, [] {
     for (const void* f : {reinterpret_cast<const void*>(&k_route<8>), reinterpret_cast<const void*>(&k_route<16>),
-                          reinterpret_cast<const void*>(&k_route<32>)})
-      (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)route_lds_bytes(1024));
+                          reinterpret_cast<const void*>(&k_route<32>)}) {
+      const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)route_lds_bytes(1024));
+      if (e != hipSuccess && attr_err == hipSuccess) attr_err = e;
+    }
   });
+  if (attr_err != hipSuccess) {
+    note_hip_error(attr_err);
+    return;
+  }
   RouteArgs a{};
   a.ids = ids; a.T = T; a.k = k; a.E = E;
   a.ntiles = T > 0 ? (int)((T + kRouteThreads - 1) / kRouteThreads) : 1;

@@ -13,7 +13,7 @@ moesq = pytest.importorskip("sparse_quantized_moe_amd")
 if not os.path.exists(moesq.library_path):
     pytest.skip("libmoesq.so not built (run python -m sparse_quantized_moe_amd.build)", allow_module_level=True)
 
-OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIP, DEVICE = 0, -1, -2, -3, -4, -5
 
 
 def declared_symbols():
@@ -37,7 +37,8 @@ def test_every_declared_symbol_is_exported():
 def test_status_strings():
     L = moesq.lib()
     for s, want in [(OK, b"ok"), (INVALID, b"invalid argument"), (UNSUPPORTED, b"unsupported shape"),
-                    (WORKSPACE, b"workspace too small"), (-4, b"HIP error")]:
+                    (WORKSPACE, b"workspace too small"), (HIP, b"HIP error"),
+                    (DEVICE, b"device-side wait ran out")]:
         assert L.moesq_status_string(s) == want
 
 
@@ -93,6 +94,15 @@ def test_argument_checks_return_status_without_launching():
     assert L.moesq_moe_ffn(*args(_weights(E=E, N=2 * I, K=H, G=1), w2, 1 << 30)) == INVALID
     assert L.moesq_moe_ffn(*args(w13, w2, 16)) == WORKSPACE
     assert L.moesq_moe_ffn(P, 0, H, P, P, 2, ctypes.byref(w13), ctypes.byref(w2), P, P, P, P, 16, 0, None) == OK
+    # 32-bit buffer offsets: the down input codes (I > H) past 2 GiB are refused, the gate/up ones fit
+    Hs, Is, Ts, ks = 256, 4096, 131072, 8                   # T*k*I/2 = 2^31, T*k*H/2 = 2^27
+    w13s = _weights(E=E, N=2 * Is, K=Hs, G=2)
+    w2s = _weights(E=E, N=Hs, K=Is, G=1)
+    assert L.moesq_moe_ffn(P, Ts, Hs, P, P, ks, ctypes.byref(w13s), ctypes.byref(w2s), P, P, P, P, 1 << 62, 0,
+                           None) == UNSUPPORTED
+    assert b"2 GiB" in L.moesq_last_error()
+    assert L.moesq_moe_ffn(P, Ts - 1, Hs, P, P, ks, ctypes.byref(w13s), ctypes.byref(w2s), P, P, P, P, 16, 0,
+                           None) == WORKSPACE                # one token fewer: past the offset check
     # router: k out of range, too many experts, bad dtype, null outputs; no tokens is a no-op
     assert L.moesq_route_topk(P, 0, 4, 8, 9, 1, P, P, None) == INVALID
     assert L.moesq_route_topk(P, 0, 4, 128, 65, 1, P, P, None) == INVALID
