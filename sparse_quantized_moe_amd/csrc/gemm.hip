@@ -499,8 +499,18 @@ __global__ __launch_bounds__(kStreamThreads) __attribute__((amdgpu_waves_per_eu(
 // ---------------------------------------------------------------------------------------------
 constexpr int kPreTG = 8;
 constexpr int kPreBMT = kPreTG * 16;
-constexpr int kPreRowStride = 256 * 2 + 16;   // bytes per token row of one 256-K step in LDS (+16 B skew)
-constexpr int kPreLdsB = kPreBMT * kPreRowStride;
+constexpr int kPreRowBytes = 256 * 2;          // one 256-K step of a token row in LDS (f16): 32 units of 16 B
+constexpr int kPreLdsB = kPreBMT * kPreRowBytes;
+
+// LDS byte offset of 16-byte unit u (0..31) of token row r in one staged step. The unit index is
+// XOR-swizzled with the row's low five bits, so that both access patterns are free of LDS bank
+// conflicts (measured on gfx950 with the hardware's conflict counter): the staging writes, where
+// consecutive lanes write one unit of consecutive rows, and the MFMA operand reads, where the 16
+// lanes of a quarter-wave read one unit of 16 consecutive rows and the quarters read units 0, 1, 8,
+// 9 (+ 2t) of them. A plain row stride of 512 + 16 bytes costs about 4 extra cycles per read.
+__device__ __forceinline__ uint32_t pre_lds_off(int row, int unit) {
+  return (uint32_t)row * kPreRowBytes + ((uint32_t)(unit ^ (row & 31)) << 4);
+}
 
 // Work placement: consecutive workgroup ids go to the 8 XCDs in turn, and each XCD has its own L2.
 // Workgroup L therefore takes item (L % 8) * per + L / 8 of the (m-block, n-block) work list, m-block
@@ -516,53 +526,59 @@ constexpr int kXcds = 8;
 // that way and keeps 4 waves (two workgroups per CU); so does the pair-bitmask layout, whose larger
 // register set would spill at 8.
 template <int EPI, int LAYOUT>
-__host__ __device__ constexpr int prefill_waves() { return EPI == kEpiGateUp && LAYOUT == 1 ? 8 : 4; }
+__host__ __device__ constexpr int prefill_waves() { return LAYOUT == 1 && EPI != kEpiStore ? 8 : 4; }
 
 template <int EPI, int NWP>
 __host__ __device__ constexpr int prefill_nblocks(int N) {
   return EPI == kEpiGateUp ? ((N >> 1) + 32 * NWP - 1) / (32 * NWP) : (N + 64 * NWP - 1) / (64 * NWP);
 }
 
-// A workgroup owns one m-block (<= 128 rows of one expert) and 64 NWP weight rows; each wave keeps 4
-// row-tiles x 8 token tiles of accumulators and reuses every decoded weight fragment over the 8
-// token tiles. Per 256-K step the activations are converted to exact f16 in LDS; their codes are
-// prefetched into registers one step ahead (NWP / 2 threads per row, each 256 / NWP bytes of codes
-// and 16 / NWP scale bytes), and the weights run through a two-slot register ring reloaded right
-// after decode, so every global load in the K loop is a prefetch issued on every path.
-template <int EPI, int LAYOUT, int NWP>
-__global__ __launch_bounds__(NWP * 64) void k_gemm_prefill(GemmParams p) {
-  constexpr int TG = kPreTG, BMT = kPreBMT, RS = kPreRowStride;
-  constexpr int SPR = NWP * 64 / BMT;              // staging threads per row
-  constexpr int GPT = 8 / SPR;                     // 32-K groups per staging thread and step
-  static_assert(SPR * BMT == NWP * 64 && (GPT == 4 || GPT == 2), "staging map");
-  extern __shared__ __align__(16) uint8_t smem[];
-  uint8_t* sB = smem;                              // [BMT][RS] f16 of one 256-K step
-  uint16_t* lut = reinterpret_cast<uint16_t*>(smem + kPreLdsB);
-  __shared__ int s_e;
-  __shared__ int s_arow[BMT];                      // activation row of each m-block row
-  __shared__ float s_rw[BMT];                      // router weight of each row (down)
+// What a prefill workgroup knows about its item once it has found it.
+struct PrefillItem {
+  int e, row0, m0, mrows;
+  int gw;                 // wave index over the expert's weight rows
+  uint32_t ar;            // activation row this thread stages (row 0 of the block when past the block)
+  bool srow_live;
+  EpiScalars es;
+};
 
+// The K loop and epilogue of one item for TGN token tiles (TGN >= the item's live tiles, a power of
+// two): every staged step's MFMAs run over all TGN tiles with no branch, so the operand reads of one
+// tile are issued under the MFMAs of the previous one. Rows between the live rows and TGN * 16 hold
+// whatever the LDS held; their accumulator columns are computed and never stored.
+template <int EPI, int LAYOUT, int NWP, int TGN>
+__device__ __forceinline__ void prefill_item(const GemmParams& p, const PrefillItem& it, uint8_t* sB,
+                                             const uint16_t* lut, float* s_rw) {
+  constexpr int SPR = NWP * 64 / kPreBMT;          // staging threads per row
+  constexpr int GPT = 8 / SPR;                     // 32-K groups per staging thread and step
+  static_assert(SPR * kPreBMT == NWP * 64 && (GPT == 4 || GPT == 2), "staging map");
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int K = p.K;
-  const int nblocks = prefill_nblocks<EPI, NWP>(p.N);
-  const int items = p.tile_offsets[p.E] * nblocks;
-  const int per = (items + kXcds - 1) / kXcds;
-  const int xi = (int)(blockIdx.x / kXcds);
-  const int w_item = (int)(blockIdx.x % kXcds) * per + xi;
-  if (xi >= per || w_item >= items) return;
-  const int mb = w_item / nblocks, nb = w_item - mb * nblocks;
-  if (LAYOUT == 0 && tid < 256) lut[tid] = (uint16_t)smfmac_index_of_mask_byte((uint32_t)tid);
-  const int e = find_expert(p.tile_offsets, p.E, mb, &s_e);
-  if (e < 0) return;
-  const int row0 = p.offsets[e];
-  const int M = p.offsets[e + 1] - row0;
-  const int m0 = (mb - p.tile_offsets[e]) * BMT;
-  const int mrows = M - m0 < BMT ? M - m0 : BMT;
-  const int ntiles = (mrows + 15) >> 4;
-  if (tid < BMT) {
-    const int r = row0 + m0 + tid;
-    s_arow[tid] = tid < mrows ? (p.a_rows ? p.a_rows[r] : r) : 0;
-  }
+  const int nsteps = K >> 8;
+  const int nrow = lane & 15, qb = lane >> 4;
+  const int row0 = it.row0, m0 = it.m0, mrows = it.mrows;
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.a_codes), (short)0, (int)(p.rows * (K >> 1)), kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.a_scales), (short)0, (int)(p.rows * (K >> 5)), kBufferRsrcWord3);
+  const int sn = tid % kPreBMT, sh = tid / kPreBMT;
+  // staging: thread (row sn, part sh) converts groups GPT sh .. GPT sh + GPT - 1 of each step, i.e.
+  // units 4 GPT sh + (4 j + h); 4 GPT sh and 4 j + h occupy different bits, so the swizzled offset is
+  // a per-thread base XOR a constant
+  const uint32_t wbase = (uint32_t)sn * kPreRowBytes + ((uint32_t)((4 * GPT * sh) ^ (sn & 31)) << 4);
+  // operand reads: lane (nrow, qb) of tile tt reads units u0 + 2t and u0 + 2t + 16 of row tt 16 + nrow,
+  // u0 = 8 (qb / 2) + qb % 2; with x = u0 ^ nrow (bits 0-3) the unit's swizzled index is
+  // x ^ 2t ^ 16 ((tt & 1) ^ hi): per t a lane address, the rest immediate offsets
+  const uint32_t x0 = (uint32_t)((8 * (qb >> 1) + (qb & 1)) ^ nrow);
+  uint32_t roff[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) roff[t] = (uint32_t)nrow * kPreRowBytes + ((x0 ^ (uint32_t)(2 * t)) << 4);
+
+  int wrow[4];
+  const bool active = wave_rows<EPI>(p.N, 0, it.gw, wrow);
+  WeightPtrs<LAYOUT> wp;
+  wp.init(p, it.e, wrow, active, lane);
+
   // down: the rows' router weights (topk_weights[sorted[r]], two dependent loads) are loaded under
   // the K loop's first steps and staged in LDS for the epilogue only
   int rw_pair = 0;
@@ -570,40 +586,22 @@ __global__ __launch_bounds__(NWP * 64) void k_gemm_prefill(GemmParams p) {
   const bool rw_live = EPI == kEpiDown && tid < mrows;
   auto rw_first = [&]() { if (rw_live) rw_pair = p.sorted[row0 + m0 + tid]; };
   auto rw_second = [&]() { if (rw_live) rw = p.topk_weights[rw_pair]; };
-  const EpiScalars es = epi_scalars<EPI>(p, e);
 
-  int wrow[4];
-  const int gw = nb * NWP + wv;                    // wave index over the expert's weight rows
-  const bool active = wave_rows<EPI>(p.N, 0, gw, wrow);
-  WeightPtrs<LAYOUT> wp;
-  wp.init(p, e, wrow, active, lane);
-  const int nsteps = K >> 8;
-  const int nrow = lane & 15, qb = lane >> 4;
-  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(p.a_codes), (short)0, (int)(p.rows * (K >> 1)), kBufferRsrcWord3);
-  const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(p.a_scales), (short)0, (int)(p.rows * (K >> 5)), kBufferRsrcWord3);
-  // staging map: thread -> row sn, 32-K groups GPT sh .. GPT sh + GPT - 1 of each step; consecutive
-  // lanes take consecutive rows, so each 8-lane LDS write group lands on 8 rows (different banks via
-  // the skew)
-  const int sn = tid % BMT, sh = tid / BMT;
-  __syncthreads();                                 // s_arow
-  const bool srow_live = sn < mrows;
-  const uint32_t ar = (uint32_t)s_arow[srow_live ? sn : 0];
   struct Act { u32x4 v[GPT]; uint32_t s; };
   auto prefetch = [&](int gs, Act& ac) {
-    const bool live = srow_live && gs < nsteps;
-    const uint32_t cb = ar * (uint32_t)(K >> 1) + (uint32_t)(gs * 128 + sh * 16 * GPT);
+    const bool live = it.srow_live && gs < nsteps;
+    const uint32_t cb = it.ar * (uint32_t)(K >> 1) + (uint32_t)(gs * 128 + sh * 16 * GPT);
 #pragma unroll
     for (int j = 0; j < GPT; ++j)
       ac.v[j] = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, live ? cb + 16u * j : kOutOfRange, 0, 0);
-    const uint32_t so = live ? ar * (uint32_t)(K >> 5) + (uint32_t)(gs * 8 + sh * GPT) : kOutOfRange;
+    const uint32_t so = live ? it.ar * (uint32_t)(K >> 5) + (uint32_t)(gs * 8 + sh * GPT) : kOutOfRange;
     if constexpr (GPT == 4) ac.s = __builtin_amdgcn_raw_buffer_load_b32(s_rsrc, so, 0, 0);
     else ac.s = __builtin_amdgcn_raw_buffer_load_b16(s_rsrc, so, 0, 0);
   };
+  const bool stage_row = sn < ((mrows + 15) & ~15);           // rows of the live tiles (zeros past the block)
   auto commit = [&](const Act& ac) {
     __syncthreads();
-    if (sn < ntiles * 16) {
+    if (stage_row) {
 #pragma unroll
       for (int j = 0; j < GPT; ++j) {
         const f16x2 sp = j < 2 ? scale_pair_f16<false>(ac.s) : scale_pair_f16<true>(ac.s);
@@ -611,46 +609,59 @@ __global__ __launch_bounds__(NWP * 64) void k_gemm_prefill(GemmParams p) {
         u32x4 u4[4];
         act_group_kprime(ac.v[j], s2, u4);
 #pragma unroll
-        for (int h = 0; h < 4; ++h)                // LDS unit 4 (GPT sh + j) + h of the step
-          *reinterpret_cast<u32x4*>(sB + sn * RS + (4 * (GPT * sh + j) + h) * 16) = u4[h];
+        for (int h = 0; h < 4; ++h)
+          *reinterpret_cast<u32x4*>(sB + (wbase ^ ((uint32_t)(4 * j + h) << 4))) = u4[h];
       }
     }
     __syncthreads();
   };
 
-  f32x4 acc[4][TG];
+  f32x4 acc[4][TGN];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-    for (int tt = 0; tt < TG; ++tt) acc[rt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int tt = 0; tt < TGN; ++tt) acc[rt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // operand reads of tile tt for smfmac t: units u and u + 16 of row tt 16 + nrow (bit 4 of the
+  // swizzled index is (tt & 1) ^ half, an immediate offset)
+  auto readB = [&](int t, int tt, u32x4 (&b)[2]) {
+    const uint8_t* rb = sB + roff[t] + tt * 16 * kPreRowBytes;
+    b[0] = *reinterpret_cast<const u32x4*>(rb + ((tt & 1) << 8));
+    b[1] = *reinterpret_cast<const u32x4*>(rb + (((tt & 1) ^ 1) << 8));
+  };
+  auto decodeA = [&](const WeightFrag<>& w, int t, int rt, f16x8 (&A)[4], int (&idx)[4]) {
+    const f16x2 sp = scale_pair_f16(w.sc[rt]);
+    const f16x2 s2 = (t < 2) ? __builtin_shufflevector(sp, sp, 0, 0) : __builtin_shufflevector(sp, sp, 1, 1);
+    A[rt] = weight_operand_of<LAYOUT>(frag_word(w.pk[rt], t), s2);
+    idx[rt] = sparse_index<LAYOUT>(w.mk[rt], t, lut);
+  };
+  // One staged step, software-pipelined by hand: the operand reads run one tile ahead of the MFMAs
+  // (two register sets), and a scheduling fence after each tile keeps that order (left alone, the
+  // scheduler sinks the reads next to their MFMAs to save registers, and every tile waits out the
+  // LDS latency). The weight operands of smfmac t are decoded before its tiles; the other wave of the
+  // SIMD keeps the matrix unit busy meanwhile.
   auto step = [&](WeightFrag<>& w, int reload) {
-    const uint8_t* brow = sB + nrow * RS + (8 * (qb >> 1) + (qb & 1)) * 16;
+    u32x4 bb[2][2];
+    readB(0, 0, bb[0]);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       f16x8 A[4];
       int idx[4];
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        const f16x2 sp = scale_pair_f16(w.sc[rt]);
-        const f16x2 s2 = (t < 2) ? __builtin_shufflevector(sp, sp, 0, 0) : __builtin_shufflevector(sp, sp, 1, 1);
-        A[rt] = weight_operand_of<LAYOUT>(frag_word(w.pk[rt], t), s2);
-        idx[rt] = sparse_index<LAYOUT>(w.mk[rt], t, lut);
-      }
-      if (t == 3 && reload >= 0) {
+      for (int rt = 0; rt < 4; ++rt) decodeA(w, t, rt, A, idx);
+      if (t == 3 && reload >= 0) {                   // the slot's last word is decoded: reload it
         slot_decoded<4>(A, idx);
         wp.load(reload, w, active && reload < nsteps);
       }
 #pragma unroll
-      for (int tt = 0; tt < TG; ++tt) {
-        if (tt < ntiles) {
-          const uint8_t* bp = brow + tt * 16 * RS + 2 * t * 16;
-          const u32x4 b0 = *reinterpret_cast<const u32x4*>(bp);
-          const u32x4 b1 = *reinterpret_cast<const u32x4*>(bp + 16 * 16);
-          const f16x16 B = __builtin_bit_cast(f16x16, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
+      for (int tt = 0; tt < TGN; ++tt) {
+        const int cur = (t * TGN + tt) & 1;
+        if (tt + 1 < TGN) readB(t, tt + 1, bb[cur ^ 1]);
+        else if (t < 3) readB(t + 1, 0, bb[cur ^ 1]);
+        const f16x16 B = __builtin_bit_cast(f16x16, __builtin_shufflevector(bb[cur][0], bb[cur][1], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-          for (int rt = 0; rt < 4; ++rt)
-            acc[rt][tt] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(A[rt], B, acc[rt][tt], idx[rt], 0, 0);
-        }
+        for (int rt = 0; rt < 4; ++rt)
+          acc[rt][tt] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(A[rt], B, acc[rt][tt], idx[rt], 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
@@ -681,11 +692,60 @@ __global__ __launch_bounds__(NWP * 64) void k_gemm_prefill(GemmParams p) {
     step(w0, -1);
   }
   if constexpr (EPI == kEpiDown) {
-    if (tid < BMT) s_rw[tid] = rw;                 // rows past the m-block: 0
+    if (tid < kPreBMT) s_rw[tid] = rw;             // rows past the m-block: 0
     __syncthreads();
   }
   if (!active) return;
-  gemm_epilogue<EPI, TG>(p, es, acc, row0, m0, mrows, 0, gw, wrow, s_rw, lane);
+  gemm_epilogue<EPI, TGN>(p, it.es, acc, row0, m0, mrows, 0, it.gw, wrow, s_rw, lane);
+}
+
+// A workgroup owns one m-block (<= 128 rows of one expert) and 64 NWP weight rows; each wave keeps 4
+// row-tiles x up to 8 token tiles of accumulators and reuses every decoded weight fragment over the
+// token tiles. Per 256-K step the activations are converted to exact f16 in LDS; their codes are
+// prefetched into registers one step ahead (NWP / 2 threads per row, each 256 / NWP bytes of codes
+// and 16 / NWP scale bytes), and the weights run through a two-slot register ring reloaded right
+// after decode, so every global load in the K loop is a prefetch issued on every path.
+template <int EPI, int LAYOUT, int NWP>
+__global__ __launch_bounds__(NWP * 64) __attribute__((amdgpu_waves_per_eu(LAYOUT == 1 ? 8 / NWP : 1))) void k_gemm_prefill(
+    GemmParams p) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint8_t* sB = smem;                              // [BMT] rows of one 256-K step, swizzled units
+  uint16_t* lut = reinterpret_cast<uint16_t*>(smem + kPreLdsB);
+  __shared__ int s_e;
+  __shared__ int s_arow[kPreBMT];                  // activation row of each m-block row
+  __shared__ float s_rw[kPreBMT];                  // router weight of each row (down)
+
+  const int tid = threadIdx.x, wv = tid >> 6;
+  const int nblocks = prefill_nblocks<EPI, NWP>(p.N);
+  const int items = p.tile_offsets[p.E] * nblocks;
+  const int per = (items + kXcds - 1) / kXcds;
+  const int xi = (int)(blockIdx.x / kXcds);
+  const int w_item = (int)(blockIdx.x % kXcds) * per + xi;
+  if (xi >= per || w_item >= items) return;
+  const int mb = w_item / nblocks, nb = w_item - mb * nblocks;
+  if (LAYOUT == 0 && tid < 256) lut[tid] = (uint16_t)smfmac_index_of_mask_byte((uint32_t)tid);
+  PrefillItem it;
+  it.e = find_expert(p.tile_offsets, p.E, mb, &s_e);
+  if (it.e < 0) return;
+  it.row0 = p.offsets[it.e];
+  const int M = p.offsets[it.e + 1] - it.row0;
+  it.m0 = (mb - p.tile_offsets[it.e]) * kPreBMT;
+  it.mrows = M - it.m0 < kPreBMT ? M - it.m0 : kPreBMT;
+  if (tid < kPreBMT) {
+    const int r = it.row0 + it.m0 + tid;
+    s_arow[tid] = tid < it.mrows ? (p.a_rows ? p.a_rows[r] : r) : 0;
+  }
+  it.es = epi_scalars<EPI>(p, it.e);
+  it.gw = nb * NWP + wv;
+  const int sn = tid % kPreBMT;
+  __syncthreads();                                 // s_arow
+  it.srow_live = sn < it.mrows;
+  it.ar = (uint32_t)s_arow[it.srow_live ? sn : 0];
+  const int ntiles = (it.mrows + 15) >> 4;
+  if (ntiles > 4) prefill_item<EPI, LAYOUT, NWP, 8>(p, it, sB, lut, s_rw);
+  else if (ntiles > 2) prefill_item<EPI, LAYOUT, NWP, 4>(p, it, sB, lut, s_rw);
+  else if (ntiles > 1) prefill_item<EPI, LAYOUT, NWP, 2>(p, it, sB, lut, s_rw);
+  else prefill_item<EPI, LAYOUT, NWP, 1>(p, it, sB, lut, s_rw);
 }
 
 KernelEvents& kernel_events() {
