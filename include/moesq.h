@@ -176,6 +176,23 @@ moesq_status moesq_moe_ffn(const void *x, int64_t T, int32_t H, const int32_t *t
                            float *out, void *workspace, size_t workspace_bytes, uint32_t flags,
                            hipStream_t stream);
 
+/* The MoE FFN of moesq_moe_ffn without a caller workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid allocation). The
+ * workspace is a library-owned static device array of moesq_noalloc_scratch_bytes() bytes (64 MiB),
+ * one per GPU the library runs on, held until the process ends; the call allocates and frees nothing.
+ * Same arguments, results and intermediates (in that array) as moesq_moe_ffn with
+ * MOESQ_FLAG_UNFUSED: the one-launch path is not used (MOESQ_FLAG_FUSED is ignored). Every call on a
+ * GPU shares that GPU's array, which keeps the previous call's contents (no kernel of the FFN needs it
+ * cleared): calls that overlap in time on one GPU race, and must not be made. Errors: those of
+ * moesq_moe_ffn, plus MOESQ_ERR_WORKSPACE (nothing enqueued) when moesq_moe_ffn_workspace_size() of
+ * the call exceeds the array (decode batches fit: at 128 experts, hidden 2048 and intermediate 768,
+ * T*k up to about 6900 pairs), and MOESQ_ERR_HIP if the array's device address cannot be found. */
+moesq_status moesq_moe_ffn_noalloc(const void *x, int64_t T, int32_t H, const int32_t *topk_ids,
+                                   const float *topk_weights, int32_t k, const moesq_weights *w13,
+                                   const moesq_weights *w2, const float *a13_global, const float *a2_global,
+                                   float *out, uint32_t flags, hipStream_t stream);
+size_t moesq_noalloc_scratch_bytes(void);
+
 /* Router of the MoE layer (the step that feeds the permutation): per token t, softmax over the E
  * expert logits, the k most probable experts (equal probability: the lower expert id first), listed
  * by decreasing probability, and their weights: the probabilities renormalized over the k picks

@@ -38,7 +38,8 @@ EXPORTED_SYMBOLS = (
     "moesq_moe_ffn_workspace_size", "moesq_moe_ffn", "moesq_compress_weights", "moesq_validate_weights",
     "moesq_unpack_pair_bitmask", "moesq_pack_pair_bitmask", "moesq_set_stage_events", "moesq_tiled_bytes",
     "moesq_prepare_weights", "moesq_unprepare_weights", "moesq_permute_workspace_size", "moesq_probe_smfmac", "moesq_probe_read",
-    "moesq_route_topk", "moesq_fold_gate_up_globals", "moesq_set_fused_spin_limit",
+    "moesq_route_topk", "moesq_fold_gate_up_globals", "moesq_set_fused_spin_limit", "moesq_moe_ffn_noalloc",
+    "moesq_noalloc_scratch_bytes",
 )
 
 
@@ -83,6 +84,9 @@ def _declare(L: ctypes.CDLL) -> None:
         "moesq_moe_ffn_workspace_size": (_SZ, [_I64, _I32, _I32, _I32, _I32, _U32]),
         "moesq_moe_ffn": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _I32, ctypes.POINTER(_CWeights),
                                          ctypes.POINTER(_CWeights), _P, _P, _P, _P, _SZ, _U32, _P]),
+        "moesq_moe_ffn_noalloc": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _I32, ctypes.POINTER(_CWeights),
+                                                 ctypes.POINTER(_CWeights), _P, _P, _P, _U32, _P]),
+        "moesq_noalloc_scratch_bytes": (_SZ, []),
         "moesq_compress_weights": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _P, _P, _P]),
         "moesq_validate_weights": (ctypes.c_int, [_P, _I64, _I32, _P, _P]),
         "moesq_unpack_pair_bitmask": (ctypes.c_int, [_P, _P, _I64, _I32, _P, _P, _P]),
@@ -310,6 +314,24 @@ def moe_ffn(x: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.Tensor,
     return out
 
 
+def moe_ffn_noalloc(x: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.Tensor, w13: SparseWeights,
+                    w2: SparseWeights, a13_global: torch.Tensor, a2_global: torch.Tensor,
+                    out: Optional[torch.Tensor] = None, flags: int = 0) -> torch.Tensor:
+    """moesq_moe_ffn_noalloc: the FFN with the library's static device scratch as its workspace (no
+    workspace argument; pass ``out`` to keep the call itself free of allocation)."""
+    T, H = x.shape
+    k = topk_ids.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float32, device=x.device)
+    c13, c2 = w13.c_struct(), w2.c_struct()
+    _check(lib().moesq_moe_ffn_noalloc(_dev(x, "x", torch.bfloat16), T, H, _dev(topk_ids, "topk_ids", torch.int32),
+                                       _dev(topk_weights, "topk_weights", torch.float32), k, ctypes.byref(c13),
+                                       ctypes.byref(c2), _dev(a13_global, "a13_global", torch.float32),
+                                       _dev(a2_global, "a2_global", torch.float32), _dev(out, "out", torch.float32),
+                                       flags, _stream()))
+    return out
+
+
 def ffn_intermediates(workspace: torch.Tensor, T: int, H: int, I: int, k: int, E: int) -> dict:
     """Views of the intermediates a moe_ffn call left in its workspace (stream-ordered after the call).
     a13 rows are in pair order (row p = t*k + j); a2 and down rows in sorted order (row inv[p])."""
@@ -333,7 +355,7 @@ def ffn_intermediates(workspace: torch.Tensor, T: int, H: int, I: int, k: int, E
     }
 
 
-__all__.append("ffn_intermediates")
+__all__ += ["ffn_intermediates", "moe_ffn_noalloc"]
 
 
 def compress_weights(w: torch.Tensor, packed: Optional[torch.Tensor] = None, mask: Optional[torch.Tensor] = None,

@@ -26,6 +26,16 @@ hipError_t take_hip_error() {
 namespace {
 
 thread_local std::string g_last_error;
+
+}  // namespace
+
+moesq_status moesq::report(moesq_status s, const char* msg) {
+  g_last_error = msg;
+  return s;
+}
+
+namespace {
+
 thread_local int64_t g_fused_spin_limit = -1;
 thread_local hipEvent_t* g_stage_events = nullptr;
 thread_local int g_stage_n = 0;
@@ -257,10 +267,14 @@ size_t moesq_moe_ffn_workspace_size(int64_t T, int32_t H, int32_t I, int32_t k, 
   return L.total;
 }
 
-moesq_status moesq_moe_ffn(const void* x, int64_t T, int32_t H, const int32_t* topk_ids, const float* topk_weights,
-                           int32_t k, const moesq_weights* w13, const moesq_weights* w2, const float* a13_global,
-                           const float* a2_global, float* out, void* workspace, size_t workspace_bytes, uint32_t flags,
-                           hipStream_t stream) {
+}  // extern "C"
+
+// The argument checks of moesq_moe_ffn that do not involve the workspace (shared with the
+// allocation-free variant). MOESQ_OK with T == 0 means a no-op.
+moesq_status moesq::validate_ffn_args(const void* x, int64_t T, int32_t H, const int32_t* topk_ids,
+                                      const float* topk_weights, int32_t k, const moesq_weights* w13,
+                                      const moesq_weights* w2, const float* a13_global, const float* a2_global,
+                                      const float* out) {
   moesq_status s = check_weights(w13, "moe_ffn w13");
   if (s != MOESQ_OK) return s;
   s = check_weights(w2, "moe_ffn w2");
@@ -276,10 +290,23 @@ moesq_status moesq_moe_ffn(const void* x, int64_t T, int32_t H, const int32_t* t
   MOESQ_REQUIRE(T * k * ((H > I ? H : I) / 2) < ((int64_t)1 << 31), MOESQ_ERR_UNSUPPORTED,
                 "moe_ffn: the gate/up and down input codes must stay below 2 GiB (32-bit buffer offsets)");
   if (T == 0) return MOESQ_OK;
-  MOESQ_REQUIRE(x && topk_ids && topk_weights && a13_global && a2_global && out && workspace, MOESQ_ERR_INVALID,
+  MOESQ_REQUIRE(x && topk_ids && topk_weights && a13_global && a2_global && out, MOESQ_ERR_INVALID,
                 "moe_ffn: null pointer");
-  MOESQ_REQUIRE(aligned16(x) && aligned16(out) && aligned16(workspace), MOESQ_ERR_INVALID,
-                "moe_ffn: x, out and workspace must be 16-byte aligned");
+  MOESQ_REQUIRE(aligned16(x) && aligned16(out), MOESQ_ERR_INVALID, "moe_ffn: x and out must be 16-byte aligned");
+  return MOESQ_OK;
+}
+
+extern "C" {
+
+moesq_status moesq_moe_ffn(const void* x, int64_t T, int32_t H, const int32_t* topk_ids, const float* topk_weights,
+                           int32_t k, const moesq_weights* w13, const moesq_weights* w2, const float* a13_global,
+                           const float* a2_global, float* out, void* workspace, size_t workspace_bytes, uint32_t flags,
+                           hipStream_t stream) {
+  moesq_status s = moesq::validate_ffn_args(x, T, H, topk_ids, topk_weights, k, w13, w2, a13_global, a2_global, out);
+  if (s != MOESQ_OK || T == 0) return s;
+  const int32_t E = w13->E, I = w2->K;
+  MOESQ_REQUIRE(workspace, MOESQ_ERR_INVALID, "moe_ffn: null pointer");
+  MOESQ_REQUIRE(aligned16(workspace), MOESQ_ERR_INVALID, "moe_ffn: x, out and workspace must be 16-byte aligned");
   moesq_ffn_layout L;
   moesq_moe_ffn_layout(T, H, I, k, E, flags, &L);
   MOESQ_REQUIRE(workspace_bytes >= L.total, MOESQ_ERR_WORKSPACE, "moe_ffn: workspace too small");

@@ -4,6 +4,8 @@
 #include <hip/hip_ext.h>
 #include <stdint.h>
 
+#include "moesq.h"
+
 namespace moesq {
 
 // Rows of x (gathered through src_row when given) quantized with global[0], or with global[e] for
@@ -124,6 +126,13 @@ void launch_probe_read(const void* src, int64_t bytes, uint32_t* sink, hipStream
 // the launch is skipped and the error is reported by the calling entry point (thread-local).
 void note_hip_error(hipError_t e);
 hipError_t take_hip_error();
+// Records msg as this thread's moesq_last_error() text and returns s.
+moesq_status report(moesq_status s, const char* msg);
+// The argument checks of moesq_moe_ffn that do not involve its workspace (MOESQ_OK with T == 0: a
+// no-op); they touch no device.
+moesq_status validate_ffn_args(const void* x, int64_t T, int32_t H, const int32_t* topk_ids, const float* topk_weights,
+                               int32_t k, const moesq_weights* w13, const moesq_weights* w2, const float* a13_global,
+                               const float* a2_global, const float* out);
 
 // out[t][:] = sum_j D[inv[t*k + j]][:] (rows with inv < 0 skipped), in j order.
 void launch_combine(const float* D, const int* inv, int64_t T, int k, int H, float* out, hipStream_t stream);

@@ -103,6 +103,18 @@ def test_argument_checks_return_status_without_launching():
     assert b"2 GiB" in L.moesq_last_error()
     assert L.moesq_moe_ffn(P, Ts - 1, Hs, P, P, ks, ctypes.byref(w13s), ctypes.byref(w2s), P, P, P, P, 16, 0,
                            None) == WORKSPACE                # one token fewer: past the offset check
+    # the allocation-free variant: its static scratch bounds the call (checked before any device call)
+    assert L.moesq_noalloc_scratch_bytes() == 64 << 20
+    w13d = _weights(E=128, N=2 * 768, K=2048, G=2)
+    w2d = _weights(E=128, N=2048, K=768, G=1)
+    assert L.moesq_moe_ffn_workspace_size(1024, 2048, 768, 8, 128, 0) > 64 << 20
+    assert L.moesq_moe_ffn_noalloc(P, 1024, 2048, P, P, 8, ctypes.byref(w13d), ctypes.byref(w2d), P, P, P, 0,
+                                   None) == WORKSPACE
+    assert b"static scratch" in L.moesq_last_error()
+    assert L.moesq_moe_ffn_noalloc(P, 8, 2048, P, P, 8, ctypes.byref(w13d), ctypes.byref(w2_bad), P, P, P, 0,
+                                   None) == INVALID          # the checks of moesq_moe_ffn
+    assert L.moesq_moe_ffn_noalloc(P, 0, 2048, P, P, 8, ctypes.byref(w13d), ctypes.byref(w2d), P, P, P, 0,
+                                   None) == OK               # T = 0: a no-op
     # router: k out of range, too many experts, bad dtype, null outputs; no tokens is a no-op
     assert L.moesq_route_topk(P, 0, 4, 8, 9, 1, P, P, None) == INVALID
     assert L.moesq_route_topk(P, 0, 4, 128, 65, 1, P, P, None) == INVALID
