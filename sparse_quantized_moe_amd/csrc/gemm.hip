@@ -28,9 +28,9 @@
 //     workgroup walks several n-blocks with its weight ring running across their boundaries.
 //   * k_gemm_decode_stream (small batches, gate/up, tiled weights, K <= 2048): the whole K staged once
 //     for 12 waves that each stream 32 intermediate columns.
-//   * k_gemm_prefill (large batches): a workgroup owns 128 rows x 256 weight rows; per 256-K step it
-//     dequantizes the activations into LDS as f16 and each wave reuses every decoded weight fragment
-//     over 8 token tiles.
+//   * k_gemm_prefill (large batches): a workgroup owns 128 rows x 64 NWP weight rows (512 on tiled
+//     weights); per 256-K step it dequantizes the activations into LDS as f16 and each wave reuses
+//     every decoded weight fragment over up to 8 token tiles.
 #include <atomic>
 
 #include "gemm_common.h"
@@ -519,12 +519,12 @@ __device__ __forceinline__ uint32_t pre_lds_off(int row, int unit) {
 // one expert (same weights) run side by side on one L2 instead of being fetched by every XCD.
 constexpr int kXcds = 8;
 
-// Waves per prefill workgroup (each 4 row-tiles of 16 weight rows) and the n-blocks they make. The
-// gate/up GEMM on tiled weights runs 8 waves (512 weight rows, one workgroup per CU): each staged
-// activation step then feeds twice the weight rows, which took its time from 290 to 283 us on the
-// 128-expert layer and from 513 to 486 us on the 512-expert layer. The down GEMM was 4-5 % slower
-// that way and keeps 4 waves (two workgroups per CU); so does the pair-bitmask layout, whose larger
-// register set would spill at 8.
+// Waves per prefill workgroup (each 4 row-tiles of 16 weight rows) and the n-blocks they make. Both
+// FFN GEMMs on tiled weights run 8 waves (512 weight rows, one workgroup per CU): each staged
+// activation step then feeds twice the weight rows, which took the gate/up GEMM from 290 to 283 us on
+// the 128-expert layer and from 513 to 486 us on the 512-expert layer. The plain store epilogue and
+// the pair-bitmask layout keep 4 waves (two workgroups per CU): their larger register sets would spill
+// at 8.
 template <int EPI, int LAYOUT>
 __host__ __device__ constexpr int prefill_waves() { return LAYOUT == 1 && EPI != kEpiStore ? 8 : 4; }
 
