@@ -604,6 +604,46 @@ def test_moe_ffn_fused_matches_separate_launches(case):
     assert int(it_f["status"][0]) == int(((ids < -1) | (ids >= E)).sum())
 
 
+@pytest.mark.parametrize("T", [64, 1024])
+def test_moe_ffn_graph_replay_matches_eager(T):
+    """A moe_ffn call captured into a HIP graph (no allocation, memset or host synchronization on its
+    path) replays to the eager result bit for bit, three times over, with other eager work of the
+    program (another FFN call on other inputs, a torch product) and synchronizations between the
+    replays. T = 64 runs the decode kernels, T = 1024 the large-batch ones (several routing tiles)."""
+    E, H, I, k = 8, 512, 256, 4
+    w13, w2, dense_expert = _layer(61, E, H, I)
+    x = synth.activations(62, T, H, device=DEV)
+    ids, wts = synth.routing(63, T, E, k)
+    g13, g2 = _globals(x, ids, E, dense_expert)
+    x2 = synth.activations(64, T, H, device=DEV)
+    ids2, wts2 = synth.routing(65, T, E, k)
+    args = (torch.from_numpy(ids).to(DEV), torch.from_numpy(wts).to(DEV), w13, w2,
+            torch.from_numpy(g13).to(DEV), torch.from_numpy(g2).to(DEV))
+    args2 = (torch.from_numpy(ids2).to(DEV), torch.from_numpy(wts2).to(DEV), w13, w2,
+             torch.from_numpy(g13).to(DEV), torch.from_numpy(g2).to(DEV))
+    ref = moesq.moe_ffn(x, *args).cpu()
+    ref2 = moesq.moe_ffn(x2, *args2).cpu()
+    ws = torch.empty(moesq.ffn_layout(T, H, I, k, E)["total"], dtype=torch.uint8, device=DEV)
+    out = torch.full((T, H), float("nan"), dtype=torch.float32, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        moesq.moe_ffn(x, *args, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moesq.moe_ffn(x, *args, out=out, workspace=ws)
+    a = torch.randn(256, 256, device=DEV)
+    for i in range(3):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.cpu(), ref), i
+        assert torch.equal(moesq.moe_ffn(x2, *args2).cpu(), ref2), i     # eager work between replays
+        a = a @ a.T / 256.0
+        torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("flags", [0, moesq.FLAG_FUSED])
 def test_stage_events_time_the_kernels(flags):
     """moesq_set_stage_events with 13 events: the five stage events bracket the stages and every
