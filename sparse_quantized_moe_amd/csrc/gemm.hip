@@ -542,9 +542,9 @@ struct PrefillItem {
   EpiScalars es;
 };
 
-// The K loop and epilogue of one item for TGN token tiles (TGN >= the item's live tiles, a power of
-// two): every staged step's MFMAs run over all TGN tiles with no branch, so the operand reads of one
-// tile are issued under the MFMAs of the previous one. Rows between the live rows and TGN * 16 hold
+// The K loop and epilogue of one item for TGN token tiles (TGN = the item's live tiles, 1 to 8): every
+// staged step's MFMAs run over all TGN tiles with no branch, so the operand reads of one tile are
+// issued under the MFMAs of the previous one. Rows between the live rows and TGN * 16 hold
 // whatever the LDS held; their accumulator columns are computed and never stored.
 template <int EPI, int LAYOUT, int NWP, int TGN>
 __device__ __forceinline__ void prefill_item(const GemmParams& p, const PrefillItem& it, uint8_t* sB,
@@ -741,11 +741,19 @@ __global__ __launch_bounds__(NWP * 64) __attribute__((amdgpu_waves_per_eu(LAYOUT
   __syncthreads();                                 // s_arow
   it.srow_live = sn < it.mrows;
   it.ar = (uint32_t)s_arow[it.srow_live ? sn : 0];
-  const int ntiles = (it.mrows + 15) >> 4;
-  if (ntiles > 4) prefill_item<EPI, LAYOUT, NWP, 8>(p, it, sB, lut, s_rw);
-  else if (ntiles > 2) prefill_item<EPI, LAYOUT, NWP, 4>(p, it, sB, lut, s_rw);
-  else if (ntiles > 1) prefill_item<EPI, LAYOUT, NWP, 2>(p, it, sB, lut, s_rw);
-  else prefill_item<EPI, LAYOUT, NWP, 1>(p, it, sB, lut, s_rw);
+  // one variant per live tile count: a last m-block of 5 to 7 tiles would spend 3/8 to 1/8 of a
+  // rounded-up variant's MFMAs on rows past the block (on the 512-expert, top-10 prefill layer every
+  // expert holds 54 to 112 rows, and rounding up to 4 or 8 tiles computed 44 % more tiles)
+  switch ((it.mrows + 15) >> 4) {
+    case 8: prefill_item<EPI, LAYOUT, NWP, 8>(p, it, sB, lut, s_rw); break;
+    case 7: prefill_item<EPI, LAYOUT, NWP, 7>(p, it, sB, lut, s_rw); break;
+    case 6: prefill_item<EPI, LAYOUT, NWP, 6>(p, it, sB, lut, s_rw); break;
+    case 5: prefill_item<EPI, LAYOUT, NWP, 5>(p, it, sB, lut, s_rw); break;
+    case 4: prefill_item<EPI, LAYOUT, NWP, 4>(p, it, sB, lut, s_rw); break;
+    case 3: prefill_item<EPI, LAYOUT, NWP, 3>(p, it, sB, lut, s_rw); break;
+    case 2: prefill_item<EPI, LAYOUT, NWP, 2>(p, it, sB, lut, s_rw); break;
+    default: prefill_item<EPI, LAYOUT, NWP, 1>(p, it, sB, lut, s_rw); break;
+  }
 }
 
 KernelEvents& kernel_events() {

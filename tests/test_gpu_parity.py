@@ -285,6 +285,7 @@ def test_prepare_layout_and_round_trip():
     (4, 256, 512, 2, [0, 5, 33, 17]),                             # ragged, an empty expert, decode tactic
     (3, 320, 768, 1, [200, 0, 130]),                              # prefill tactic, N not a multiple of 256
     (2, 64, 2048, 2, [1, 129]),
+    (9, 256, 512, 1, [13, 29, 45, 61, 77, 93, 109, 125, 135]),    # prefill, last m-blocks of 1 .. 8 token tiles
     (5, 128, 1280, 1, [40, 3, 0, 31, 64]),                        # decode, K-chunks of 512 with a short last one
     (6, 576, 768, 1, [7, 0, 40, 16, 1, 33]),                      # decode, K in one chunk: n-block loop, ragged
                                                                   # last n-block, several m-blocks
