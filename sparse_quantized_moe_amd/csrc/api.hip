@@ -205,7 +205,7 @@ moesq_status moesq_permute(const int32_t* topk_ids, int64_t T, int32_t k, int32_
   return check_launch(stream, false);
 }
 
-size_t moesq_grouped_gemm_workspace_size(int32_t E) { return align256((size_t)(E + 1) * 4); }
+size_t moesq_grouped_gemm_workspace_size(int32_t E) { return align256((size_t)(E + 1 + moesq::kPrefillPools) * 4); }
 
 moesq_status moesq_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global,
                                 const int32_t* expert_offsets, int64_t rows, const moesq_weights* w, float* out,
@@ -243,7 +243,7 @@ moesq_status moesq_moe_ffn_layout(int64_t T, int32_t H, int32_t I, int32_t k, in
   auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
   L->counts = take((size_t)E * 4);
   L->offsets = take((size_t)(E + 1) * 4);
-  L->tile_offsets = take((size_t)(E + 1) * 4);
+  L->tile_offsets = take((size_t)(E + 1 + moesq::kPrefillPools) * 4);
   L->status = take(4);
   L->sorted = take(P * 4);
   L->inv = take(P * 4);

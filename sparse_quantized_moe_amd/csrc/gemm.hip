@@ -518,6 +518,13 @@ __device__ __forceinline__ uint32_t pre_lds_off(int row, int unit) {
 // range of the list, so the n-blocks of one m-block (same activations) and consecutive m-blocks of
 // one expert (same weights) run side by side on one L2 instead of being fetched by every XCD.
 constexpr int kXcds = 8;
+// The prefill items (m-block major) are dealt to the XCDs in contiguous shares of equal count, so
+// that the items running at once on one XCD share activation rows and experts' weights in its L2,
+// except the last 1 / kPrefillPoolDiv of them: workgroups past their XCD's share claim those from a
+// counter, so XCDs whose shares cost less (routing skew makes items of 1 and of 8 token tiles) take
+// more of them. On the 384-expert layer equal-count shares alone left the slowest XCD about 6 %
+// behind the mean.
+constexpr int kPrefillPoolDiv = 16;
 
 // Waves per prefill workgroup (each 4 row-tiles of 16 weight rows) and the n-blocks they make. Both
 // FFN GEMMs on tiled weights run 8 waves (512 weight rows, one workgroup per CU): each staged
@@ -712,16 +719,28 @@ __global__ __launch_bounds__(NWP * 64) __attribute__((amdgpu_waves_per_eu(LAYOUT
   uint8_t* sB = smem;                              // [BMT] rows of one 256-K step, swizzled units
   uint16_t* lut = reinterpret_cast<uint16_t*>(smem + kPreLdsB);
   __shared__ int s_e;
+  __shared__ int s_pool;                           // the claimed pooled item
   __shared__ int s_arow[kPreBMT];                  // activation row of each m-block row
   __shared__ float s_rw[kPreBMT];                  // router weight of each row (down)
 
   const int tid = threadIdx.x, wv = tid >> 6;
   const int nblocks = prefill_nblocks<EPI, NWP>(p.N);
   const int items = p.tile_offsets[p.E] * nblocks;
-  const int per = (items + kXcds - 1) / kXcds;
-  const int xi = (int)(blockIdx.x / kXcds);
-  const int w_item = (int)(blockIdx.x % kXcds) * per + xi;
-  if (xi >= per || w_item >= items) return;
+  const int pooled = items / kPrefillPoolDiv;
+  const int shared_items = items - pooled;
+  const int per = (shared_items + kXcds - 1) / kXcds;
+  const int xcd = (int)(blockIdx.x % kXcds), xi = (int)(blockIdx.x / kXcds);
+  const int share_end = (xcd + 1) * per < shared_items ? (xcd + 1) * per : shared_items;
+  int w_item = xcd * per + xi;
+  if (w_item >= share_end) {                       // past the XCD's share: the next pooled item
+    // at most a quarter of the pool per XCD claims; the grid's other workgroups (sized for an upper
+    // bound of the items) exit without touching the counter
+    if (w_item - share_end >= (pooled + 3) / 4) return;
+    if (tid == 0) s_pool = atomicAdd(prefill_pools(p.tile_offsets, p.E) + (EPI == kEpiDown ? 1 : 0), 1);
+    __syncthreads();
+    w_item = shared_items + s_pool;
+    if (w_item >= items) return;
+  }
   const int mb = w_item / nblocks, nb = w_item - mb * nblocks;
   if (LAYOUT == 0 && tid < 256) lut[tid] = (uint16_t)smfmac_index_of_mask_byte((uint32_t)tid);
   PrefillItem it;
@@ -846,7 +865,11 @@ static void launch_prefill(const GemmParams& p, hipStream_t stream) {
   // spreads the live items over the XCDs and the rest of the grid exits
   const int64_t mblocks = (p.rows + kPreBMT - 1) / kPreBMT + p.E;
   const int nblocks = prefill_nblocks<EPI, NWP>(p.N);
-  const int64_t grid = ((mblocks * nblocks + kXcds - 1) / kXcds) * kXcds;
+  // per XCD: its share of an upper bound of the live items, then enough workgroups to claim up to a
+  // quarter of the pooled items (the rest of those find the pool empty and exit)
+  const int64_t bound = mblocks * nblocks;
+  const int64_t per_xcd = (bound + kXcds - 1) / kXcds + (bound + 4 * kPrefillPoolDiv - 1) / (4 * kPrefillPoolDiv);
+  const int64_t grid = per_xcd * kXcds;
   launch_kernel(k_gemm_prefill<EPI, LAYOUT, NWP>, dim3((unsigned)grid), dim3(NWP * 64), lds, stream, p);
 }
 

@@ -42,6 +42,14 @@ void launch_route(const int* ids, int64_t T, int k, int E, int* counts, int* off
 // tile_offsets from offsets for m-blocks of bm rows.
 void launch_tile_offsets(const int* offsets, int E, int bm, int* tile_offsets, hipStream_t stream);
 
+// The prefill GEMMs hand the last items out through claim counters that follow the E + 1 m-block
+// offsets: one for the GEMM of a plain or gate/up call, one for the down GEMM. Every launch that
+// writes tile_offsets zeroes them, so tile_offsets needs E + 1 + kPrefillPools ints.
+constexpr int kPrefillPools = 2;
+__host__ __device__ inline int* prefill_pools(const int* tile_offsets, int E) {
+  return const_cast<int*>(tile_offsets) + E + 1;
+}
+
 // Grouped sparse GEMM variants.
 enum { kEpiStore = 0, kEpiGateUp = 1, kEpiDown = 2 };
 enum { kTacticDecode = 0, kTacticPrefill = 1 };

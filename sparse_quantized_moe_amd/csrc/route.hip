@@ -219,6 +219,7 @@ __device__ void route_tile(const RouteArgs& a, int tile, uint8_t* smem) {
     if (a.bm > 0) a.tile_offsets[E] = totals.y;
     a.status[0] = s_bad;
   }
+  if (a.bm > 0 && tid < kPrefillPools) prefill_pools(a.tile_offsets, E)[tid] = 0;
   // scatter: through LDS when the pairs fit (scattered LDS writes, then contiguous global writes),
   // else straight to memory
   const int64_t P = a.T * k;
@@ -358,6 +359,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_scan(RouteArgs a) {
     if (a.bm > 0) a.tile_offsets[e] = tcnt[e];
     for (int t = 0; t < a.ntiles; ++t) a.tile_counts[(int64_t)t * E + e] += cnt[e];
   }
+  if (a.bm > 0 && tid < kPrefillPools) prefill_pools(a.tile_offsets, E)[tid] = 0;
   if (tid == 0) {
     a.offsets[E] = total;
     if (a.bm > 0) a.tile_offsets[E] = ttotal;
@@ -446,6 +448,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_tile_offsets(const int* offse
   const int total = route_block_scan(c, E, tmp);
   for (int e = threadIdx.x; e < E; e += kRouteThreads) tile_offsets[e] = c[e];
   if (threadIdx.x == 0) tile_offsets[E] = total;
+  if (threadIdx.x < kPrefillPools) prefill_pools(tile_offsets, E)[threadIdx.x] = 0;
 }
 
 void launch_tile_offsets(const int* offsets, int E, int bm, int* tile_offsets, hipStream_t stream) {
