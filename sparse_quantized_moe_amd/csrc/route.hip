@@ -307,18 +307,29 @@ __device__ __forceinline__ void route_quantize(const RouteArgs& a, int qb, float
       mb = __builtin_elementwise_max(mb, __float_as_uint(v[i]) & 0x7FFFFFFFu);
     }
     const bool finite = mb < 0x7F800000u;
+    // The codes and the scale of a group depend on its values and the expert's global only, so an
+    // expert whose global has the same bits as the last one encoded reuses that encoding (layers
+    // whose experts share one activation global encode each group once per run instead of once per
+    // expert).
+    bool have = false;
+    uint32_t glast = 0u;
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    int sc = 0;
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
       const int e = ids[j];
       if (j >= nrun || e < 0 || e >= a.E) continue;
       const int64_t p = p0 + j;
       const float g = s_g[e];
-      const int sc = scale_code(amax, g);
-      const float s = e4m3_value(sc);
-      const Nvfp4Snap sn = nvfp4_snap(s, g, finite);
-      uint32_t w[4];
+      if (!have || __float_as_uint(g) != glast) {
+        sc = scale_code(amax, g);
+        const float s = e4m3_value(sc);
+        const Nvfp4Snap sn = nvfp4_snap(s, g, finite);
 #pragma unroll
-      for (int h = 0; h < 4; ++h) w[h] = nvfp4_codes_snap<8>(v + 8 * h, s, g, sn);
+        for (int h = 0; h < 4; ++h) w[h] = nvfp4_codes_snap<8>(v + 8 * h, s, g, sn);
+        have = true;
+        glast = __float_as_uint(g);
+      }
       *reinterpret_cast<u32x4*>(a.codes + p * (a.H >> 1) + grp * 16) = u32x4{w[0], w[1], w[2], w[3]};
       a.scales[p * G + grp] = (uint8_t)sc;
     }
