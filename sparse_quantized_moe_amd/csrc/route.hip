@@ -351,12 +351,20 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_scan(RouteArgs a) {
   int* tcnt = cnt + a.E;                        // [E]
   __shared__ int tmp[kRouteWaves + 1];
   const int E = a.E, tid = threadIdx.x;
+  // the tile counts of an expert are read kScanBatch at a time (independent loads, one round trip
+  // per batch rather than per tile), then rewritten as exclusive prefixes
+  constexpr int kScanBatch = 16;
   for (int e = tid; e < E; e += kRouteThreads) {
     int run = 0;
-    for (int t = 0; t < a.ntiles; ++t) {
-      const int c = a.tile_counts[(int64_t)t * E + e];
-      a.tile_counts[(int64_t)t * E + e] = run;
-      run += c;
+    for (int t0 = 0; t0 < a.ntiles; t0 += kScanBatch) {
+      int c[kScanBatch];
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) c[i] = t0 + i < a.ntiles ? a.tile_counts[(int64_t)(t0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) {
+        if (t0 + i < a.ntiles) a.tile_counts[(int64_t)(t0 + i) * E + e] = run;
+        run += c[i];
+      }
     }
     cnt[e] = run;
     a.counts[e] = run;
@@ -368,7 +376,14 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_scan(RouteArgs a) {
   for (int e = tid; e < E; e += kRouteThreads) {
     a.offsets[e] = cnt[e];
     if (a.bm > 0) a.tile_offsets[e] = tcnt[e];
-    for (int t = 0; t < a.ntiles; ++t) a.tile_counts[(int64_t)t * E + e] += cnt[e];
+    for (int t0 = 0; t0 < a.ntiles; t0 += kScanBatch) {
+      int c[kScanBatch];
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) c[i] = t0 + i < a.ntiles ? a.tile_counts[(int64_t)(t0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i)
+        if (t0 + i < a.ntiles) a.tile_counts[(int64_t)(t0 + i) * E + e] = c[i] + cnt[e];
+    }
   }
   if (a.bm > 0 && tid < kPrefillPools) prefill_pools(a.tile_offsets, E)[tid] = 0;
   if (tid == 0) {
