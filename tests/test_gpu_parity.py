@@ -388,6 +388,31 @@ def test_moe_ffn_small(E, H, I, T, k, fixed, tiled):
     print("ffn small", E, H, I, T, k, st)
 
 
+@pytest.mark.parametrize("E,H,I,T,k,zipf_beta", [
+    (1, 256, 256, 300, 1, 0.0),             # one expert, top-1: m-blocks of 8, 8 and 3 token tiles
+    (3, 768, 512, 700, 2, 1.0),             # skewed, I < H, three gate/up steps
+    (17, 1280, 768, 1000, 5, 0.0),          # odd expert count, k = 5, a partial 512-row n-block
+    (5, 256, 1024, 400, 3, 1.0),            # I > H: the down GEMM's K is four times the gate/up one's
+    (40, 512, 256, 600, 10, 0.0),           # top-10 (the 16-wide routing variant) at the prefill tactic
+    (64, 512, 256, 3000, 8, 2.0),           # 15 empty experts, every tile count, a claimed item tail
+])
+def test_moe_ffn_odd_shapes(E, H, I, T, k, zipf_beta):
+    """Shapes off the beaten track through the large-batch path: every m-block tile count, a claimed
+    tail of the item list, experts with no rows, k not a power of two, I above H."""
+    from ffn_check import compare_ffn, oracle_layer
+    w13, w2, dense_expert = _layer(31, E, H, I, True)
+    x = synth.activations(32, T, H, device=DEV)
+    ids, wts = synth.routing(33, T, E, k, "zipf" if zipf_beta else "softmax", 1.0, zipf_beta)
+    g13, g2 = _globals(x, ids, E, dense_expert)
+    out, inter = _run_ffn(x, ids, wts, w13, w2, g13, g2)
+    rc, ro, rs, ri = moe.permute(ids, E)
+    assert np.array_equal(inter["offsets"], ro) and np.array_equal(inter["inv"], ri)
+    assert np.array_equal(inter["sorted"][:int(ro[-1])], rs)
+    ow13, ow2 = oracle_layer(dense_expert, range(E))
+    st = compare_ffn(x.float().cpu().numpy(), ids, wts, ow13, ow2, g13, g2, out, inter)
+    print("ffn odd shape", E, H, I, T, k, zipf_beta, st)
+
+
 _RUNS = {}
 
 
