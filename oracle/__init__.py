@@ -18,9 +18,12 @@ decision where an integer (a code or a scale byte) is decided by a real-valued c
 Parity status: the codecs, the quantizer, the codec of the storage format, the prune, the permutation,
 the grouped GEMM, the router and the gate/up fold are pinned by tests against textbook tables, a
 library cast, exact-rational brute force, rank counts, closed forms, hand-derived fixtures and the
-pages' storage figures. ``moe.moe_ffn``: parity unpinned as a whole -- it is a composition of the
-pinned stages plus libm ``exp``, and beyond that only metamorphic relations hold it (top-1 equals the
-single-expert FFN, token shuffles permute the rows, top-k is the weighted sum of top-1 runs); the
-pages print no worked FFN example.
+pages' storage figures. ``moe.moe_ffn`` is pinned against an exact evaluation written independently
+of it (exact rationals, silu to 60 digits, nearest-value search over the format tables) on a small
+layer whose down-input globals put quantization decisions next to rounding boundaries, and by
+metamorphic relations (top-1 equals the single-expert FFN, token shuffles permute the rows, top-k is
+the weighted sum of top-1 runs); ``moe.h_error_bound``, ``nvfp4.check_admissible`` and
+``nvfp4.ambiguous_groups`` by fp32 accumulations in several orders, constructed boundary cases and
+brute force. The pages print no worked FFN example.
 """
 from . import nvfp4, pairbitmask, compress, moe  # noqa: F401
